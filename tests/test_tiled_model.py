@@ -1,0 +1,98 @@
+"""The tiled schedule (fp64 CPU model) reaches the oracle's result up to summation order.
+
+The lecture notes report 8.9e-16 (no mask) / 1.0e-15 (causal) for tiled vs standard in
+float64, about 1e-15 for backward gradients, and ~1e-16 for merging 1-64 decode splits
+(tests/golden/lecture21_pins.json); the bounds below are a few times those figures to
+allow for the different sizes.
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import attention as ora
+import tiled_model as tm
+import workloads
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "lecture21_pins.json")))["pins"]
+
+
+def _head(seed, n, d, nk=None):
+    inp = workloads.make_attention_inputs(1, n, nk or n, 1, 1, d, seed=seed, dtype=workloads.F32, with_do=True)
+    return [inp[x][0, :, 0].astype(np.float64) for x in ("q", "k", "v", "do")]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n,d,br,bc", [(300, 64, 128, 64), (257, 32, 64, 128), (64, 16, 128, 64)])
+def test_tiled_forward_matches_oracle(causal, n, d, br, bc):
+    q, k, v, _ = _head(n + d, n, d)
+    scale = 1.0 / math.sqrt(d)
+    o0, l0 = ora.head_forward(q, k, v, scale, causal)
+    nblk = -(-n // br)
+    order = list(range(nblk))[::-1] if causal else None  # longest-first
+    o1, l1 = tm.fwd_tiled(q, k, v, scale, causal, br, bc, order)
+    bound = 20 * GOLD["tiled_exactness_fp64"]["causal" if causal else "no_mask"]
+    assert np.abs(o1 - o0).max() < bound
+    assert np.abs(l1 - l0).max() < 1e-13
+
+
+def test_tiled_forward_nq_ne_nk():
+    q, k, v, _ = _head(9, 100, 32, nk=333)
+    o0, l0 = ora.head_forward(q, k, v, 0.2, False)
+    o1, l1 = tm.fwd_tiled(q, k, v, 0.2, False, 64, 64)
+    assert np.abs(o1 - o0).max() < 1e-14 and np.abs(l1 - l0).max() < 1e-13
+
+
+@pytest.mark.parametrize("n,chunk", [(1, 64), (777, 64), (1000, 1000), (4096, 64)])
+def test_split_kv_merge_any_order(n, chunk):
+    g = np.random.Generator(np.random.PCG64(n))
+    q = g.standard_normal((4, 32))
+    k = g.standard_normal((n, 32))
+    v = g.standard_normal((n, 32))
+    scale = 1.0 / math.sqrt(32)
+    parts = tm.decode_partials(q, k, v, n, scale, chunk)
+    assert 1 <= len(parts) <= 64
+    o0, l0 = ora.head_forward(q, k, v, scale, False)
+    # left fold, reversed fold, shuffled fold and a pairwise tree all agree with the oracle
+    orders = [parts, parts[::-1], [parts[i] for i in g.permutation(len(parts))]]
+    results = []
+    for ps in orders:
+        acc = ps[0]
+        for p in ps[1:]:
+            acc = tm.merge(acc, p)
+        results.append(tm.finish(acc))
+    level = parts
+    while len(level) > 1:
+        level = [tm.merge(*level[i : i + 2]) if i + 1 < len(level) else level[i] for i in range(0, len(level), 2)]
+    results.append(tm.finish(level[0]))
+    for o1, l1 in results:
+        assert np.abs(o1 - o0).max() < 10 * GOLD["split_merge_exactness_fp64"]["max"]
+        assert np.abs(l1 - l0).max() < 1e-13
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_tiled_backward_matches_oracle(causal):
+    n, d = 200, 32
+    q, k, v, do = _head(77, n, d)
+    scale = 1.0 / math.sqrt(d)
+    _, lse = ora.head_forward(q, k, v, scale, causal)
+    g0 = ora.head_backward(q, k, v, do, scale, causal)
+    g1 = tm.bwd_tiled(q, k, v, do, lse, scale, causal, br=64, bc=128)
+    for a, b in zip(g0, g1):
+        assert np.abs(a - b).max() < 10 * GOLD["backward_exactness_fp64"]["max"]
+
+
+def test_causal_tile_count_pin():
+    # whole-tile skip at N=1024 with 64x64 tiles computes T(T+1)/2 of T^2 tiles
+    pin = GOLD["causal_tiles_n1024_block64"]
+    T = 1024 // 64
+    computed = sum(1 for i, j in itertools.product(range(T), range(T)) if j * 64 <= i * 64 + 63)
+    assert computed == pin["computed"] and T * T == pin["total"]
+    flop = GOLD["causal_mflop_n1024_d64_block64"]
+    full = 4 * 1024 * 1024 * 64 / 1e6
+    assert round(full, 1) == flop["full"]
+    assert round(full * computed / (T * T), 1) == flop["skipped"]
