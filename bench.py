@@ -1,0 +1,253 @@
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
+
+A step is one pass of the training-shape forward (B=16, H=16, N=2048, d=128, bf16) without
+and with the causal mask. `value` is the step's algorithmic TFLOP/s (4*N_q*N_k*d per head
+without a mask; 4*d*N(N+1)/2 with it). The same run also times the long-context causal
+forward, the ragged GQA decode (HBM GB/s) and the causal backward, each with HIP events on
+the stream the library launches on, and times the fp64 CPU oracle on a bounded sample of the
+training-shape workload (`cpu_baseline`). Inputs are the seeded synthetic tensors of
+workloads.py, resident in device memory before any timed region. One JSON line on stdout.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+METRIC = "attn fwd/bwd TFLOPS & % bf16 MFMA peak (d=128); decode HBM GB/s"
+PEAK_BF16_TFLOPS = 2516.6  # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def fwd_flops(B, H, Nq, Nk, d, causal):
+    if causal:
+        return 4.0 * B * H * d * Nq * (Nq + 1) / 2
+    return 4.0 * B * H * Nq * Nk * d
+
+
+def bwd_flops(B, H, N, d, causal):
+    # five matmuls (S recomputed, dV, dP, dK, dQ) over the visible pairs
+    pairs = N * (N + 1) / 2 if causal else N * N
+    return 10.0 * B * H * d * pairs
+
+
+def decode_bytes(w, lens):
+    kv = 2 * w.Hkv * w.d * 2 * int(np.sum(lens.astype(np.int64)))
+    return kv + w.B * w.Hq * w.d * 2 * 2 + w.B * w.Hq * 4  # + Q read, O write, L write
+
+
+def dev(x, dtype="bf16"):
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
+def time_launches(fn, reps, warmup):
+    """Per-launch durations (ms) with HIP events on the current stream (the launch stream)."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The fp64 oracle, as it stands, on whole heads of the workload until ~budget_s elapse."""
+    from oracle import attention as ora
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = 1
+    inp = workloads.make_attention_inputs(1, w.Nq, w.Nk, 4, 4, w.d, seed=w.seed, dtype=w.dtype)
+    flops, heads, t0 = 0.0, 0, time.perf_counter()
+    while True:
+        h = heads % 4
+        ora.forward(inp["q"], inp["k"], inp["v"], False, w.scale, heads=[(0, h)])
+        heads += 1
+        flops += fwd_flops(1, 1, w.Nq, w.Nk, w.d, False)
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+        "sample": f"{heads} whole heads (N_q=N_k={w.Nq}, d={w.d}, no mask) of the training-shape forward, "
+                  f"fp64 numpy, {dt:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="only the training-shape forward step")
+    ap.add_argument("--reps", type=int, default=10, help="timed launches per extra workload")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (--gpus {args.gpus} refused)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_io_aware_03_amd as fa
+
+    fa.lib()  # fail loudly if the HIP library is missing
+    torch.cuda.set_device(0)
+
+    # ---- the step: training-shape forward, without and with the causal mask ----
+    w = workloads.WORKLOADS["fwd_bf16_b16h16n2048d128"]
+    log(f"[bench] generating {w.name}")
+    inp = workloads.make_workload_inputs(w)
+    q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+    del inp
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda")
+
+    def step():
+        fa.fa_fwd(q, k, v, o, lse, causal=False, scale=w.scale)
+        fa.fa_fwd(q, k, v, o, lse, causal=True, scale=w.scale)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    step_flops = fwd_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, False) + fwd_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, True)
+    value = step_flops * args.steps / dt / 1e12
+    log(f"[bench] step: {dt / args.steps * 1e3:.3f} ms, {value:.1f} TFLOP/s")
+
+    # ---- the dominant kernel: the non-causal forward launch, HIP events on the launch stream ----
+    nc_ms = time_launches(lambda: fa.fa_fwd(q, k, v, o, lse, causal=False, scale=w.scale), args.reps * 2, 3)
+    c_ms = time_launches(lambda: fa.fa_fwd(q, k, v, o, lse, causal=True, scale=w.scale), args.reps * 2, 3)
+    nc_avg = float(np.mean(nc_ms))
+    f_nc = fwd_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, False)
+    achieved = f_nc / (nc_avg * 1e-3) / 1e12
+    results = {
+        "fwd_nc_b16h16n2048d128": {"ms": round(nc_avg, 4), "tflops": round(achieved, 2),
+                                    "frac_peak": round(achieved / PEAK_BF16_TFLOPS, 4)},
+        "fwd_causal_b16h16n2048d128": {
+            "ms": round(float(np.mean(c_ms)), 4),
+            "tflops": round(fwd_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, True) / (np.mean(c_ms) * 1e-3) / 1e12, 2),
+        },
+    }
+    results["fwd_causal_b16h16n2048d128"]["frac_peak"] = round(
+        results["fwd_causal_b16h16n2048d128"]["tflops"] / PEAK_BF16_TFLOPS, 4)
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+
+    if not args.no_extra:
+        # long-context causal forward
+        w3 = workloads.WORKLOADS["fwd_bf16_causal_h32n16384d128"]
+        log(f"[bench] {w3.name}")
+        inp = workloads.make_workload_inputs(w3)
+        q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+        del inp
+        o = torch.empty_like(q)
+        lse = torch.empty((w3.B, w3.Hq, w3.Nq), dtype=torch.float32, device="cuda")
+        ms = float(np.mean(time_launches(lambda: fa.fa_fwd(q, k, v, o, lse, causal=True, scale=w3.scale),
+                                         args.reps, 2)))
+        tf = fwd_flops(w3.B, w3.Hq, w3.Nq, w3.Nk, w3.d, True) / (ms * 1e-3) / 1e12
+        results["fwd_causal_h32n16384d128"] = {"ms": round(ms, 4), "tflops": round(tf, 2),
+                                               "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
+
+        # decode (HBM bound)
+        w4 = workloads.WORKLOADS["decode_bf16_b64hq32hkv8d128"]
+        log(f"[bench] {w4.name}")
+        inp = workloads.make_workload_inputs(w4)
+        q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+        lens = torch.from_numpy(inp["seqlens"]).cuda()
+        nbytes = decode_bytes(w4, inp["seqlens"])
+        del inp
+        o = torch.empty_like(q)
+        lse = torch.empty((w4.B, w4.Hq), dtype=torch.float32, device="cuda")
+        ws = torch.empty(fa.fa_decode_workspace_size(w4.B, w4.Hq, w4.Nk, w4.d), dtype=torch.uint8, device="cuda")
+        ms = float(np.mean(time_launches(lambda: fa.fa_decode(q, k, v, lens, o, lse, ws, scale=w4.scale),
+                                         args.reps * 2, 3)))
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        results["decode_b64hq32hkv8d128"] = {"ms": round(ms, 4), "gbs": round(gbs, 1),
+                                             "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes,
+                                             "chunk": fa.decode_chunk(w4.B, w4.Hkv, w4.Nk)}
+        del q, k, v, o, lse, ws, lens
+        torch.cuda.empty_cache()
+
+        # causal backward (pre + main + finalize), forward untimed
+        w5 = workloads.WORKLOADS["bwd_bf16_causal_b8h16n4096d128"]
+        log(f"[bench] {w5.name}")
+        inp = workloads.make_workload_inputs(w5)
+        q, k, v, do = dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["do"])
+        del inp
+        o, lse = fa.forward(q, k, v, causal=True, scale=w5.scale)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(fa.fa_bwd_workspace_size(w5.B, w5.Hq, w5.Nq, w5.d), dtype=torch.uint8, device="cuda")
+        ms = float(np.mean(time_launches(
+            lambda: fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, causal=True, scale=w5.scale), args.reps, 2)))
+        tf = bwd_flops(w5.B, w5.Hq, w5.Nq, w5.d, True) / (ms * 1e-3) / 1e12
+        results["bwd_causal_b8h16n4096d128"] = {"ms": round(ms, 4), "tflops": round(tf, 2),
+                                                "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                                                "tflops_8n2d_convention": round(0.8 * tf, 2)}
+        del q, k, v, do, o, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dt / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.Hq, "N": w.Nq, "d": w.d,
+                   "masks": ["none", "causal"], "step": "fa_fwd without + with causal mask"},
+        "roofline": {"kernel": "fwd_bf16_kernel<128,false>", "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "results": results,
+    }
+    if not args.no_cpu:
+        log("[bench] cpu baseline (fp64 oracle)")
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,205 @@
+"""Python binding of libfa, the gfx950 exact-attention library (see include/fa.h).
+
+The functions named like the C entry points (fa_fwd, fa_bwd, fa_decode) marshal torch device
+tensors into pointers, sizes and the current HIP stream and raise on a non-zero status; all
+computation happens in libfa's kernels. forward/backward/decode are conveniences that also
+allocate the outputs with torch. There is no fallback: if libfa.so is missing or fails to
+load, importing the binding's functions raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+
+FA_F32 = 0
+FA_BF16 = 1
+_STATUS = {0: "FA_OK", -1: "FA_ERR_INVALID_ARG", -2: "FA_ERR_UNSUPPORTED", -3: "FA_ERR_HIP", -4: "FA_ERR_WORKSPACE"}
+
+EXPORTED = (
+    "fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_workspace_size", "fa_strerror",
+    "fa_version", "fa_wave_efficiency", "fa_plan_splits", "fa_schedule_makespan", "fa_causal_tiles",
+    "fa_decode_chunk",
+)
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfa.so (built in-tree by exact_io_aware_03_amd.build); raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} not built; run `python -m exact_io_aware_03_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
+    L.fa_fwd.restype = i
+    L.fa_bwd_workspace_size.argtypes = [i, i, i, i]
+    L.fa_bwd_workspace_size.restype = sz
+    L.fa_bwd.argtypes = [vp] * 9 + [i] * 7 + [f, i, vp, sz, vp]
+    L.fa_bwd.restype = i
+    L.fa_decode_workspace_size.argtypes = [i, i, i, i]
+    L.fa_decode_workspace_size.restype = sz
+    L.fa_decode.argtypes = [vp] * 6 + [i] * 6 + [f, i, vp, sz, vp]
+    L.fa_decode.restype = i
+    L.fa_strerror.argtypes = [i]
+    L.fa_strerror.restype = ctypes.c_char_p
+    L.fa_version.restype = i
+    L.fa_wave_efficiency.argtypes = [i, i]
+    L.fa_wave_efficiency.restype = ctypes.c_double
+    L.fa_plan_splits.argtypes = [i, i, ctypes.c_double]
+    L.fa_plan_splits.restype = i
+    L.fa_schedule_makespan.argtypes = [ctypes.POINTER(i), i, i, i, ctypes.POINTER(i)]
+    L.fa_schedule_makespan.restype = i
+    L.fa_causal_tiles.argtypes = [i, i, i]
+    L.fa_causal_tiles.restype = ctypes.c_long
+    L.fa_decode_chunk.argtypes = [i, i, i]
+    L.fa_decode_chunk.restype = i
+    _lib = L
+    return L
+
+
+def _check(code: int):
+    if code != 0:
+        raise FAError(code, lib().fa_strerror(code).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _need_contig(*ts):
+    for t in ts:
+        if t is not None and (not t.is_contiguous() or not t.is_cuda):
+            raise ValueError("tensors must be contiguous device tensors")
+
+
+# ---- entry points with the C names (caller provides the outputs) ---------------------------
+
+def fa_fwd(q, k, v, o, lse, causal: bool = False, scale: float | None = None, stream=None) -> None:
+    """O and lse for q [B,Nq,Hq,d], k/v [B,Nk,Hkv,d] (see include/fa.h)."""
+    _need_contig(q, k, v, o, lse)
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    _check(lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, int(causal),
+                        scale, _dtype_code(q), _stream(stream)))
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool = False, scale: float | None = None,
+           stream=None) -> None:
+    _need_contig(q, k, v, o, dout, lse, dq, dk, dv, workspace)
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                        B, Hq, Hkv, Nq, Nk, d, int(causal), scale, _dtype_code(q), _ptr(workspace), ws_bytes,
+                        _stream(stream)))
+
+
+def fa_decode(q, k_cache, v_cache, seqlens, o, lse, workspace, scale: float | None = None, stream=None) -> None:
+    _need_contig(q, k_cache, v_cache, seqlens, o, lse, workspace)
+    B, Nq, Hq, d = q.shape
+    Nk_max, Hkv = k_cache.shape[1], k_cache.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().fa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o), _ptr(lse), B, Hq, Hkv,
+                           Nq, Nk_max, d, scale, _dtype_code(q), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def fa_bwd_workspace_size(B: int, Hq: int, Nq: int, d: int) -> int:
+    return int(lib().fa_bwd_workspace_size(B, Hq, Nq, d))
+
+
+def fa_decode_workspace_size(B: int, Hq: int, Nk_max: int, d: int) -> int:
+    return int(lib().fa_decode_workspace_size(B, Hq, Nk_max, d))
+
+
+# ---- allocating conveniences ---------------------------------------------------------------
+
+def forward(q, k, v, causal: bool = False, scale: float | None = None, stream=None):
+    import torch
+
+    B, Nq, Hq, _ = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    fa_fwd(q, k, v, o, lse, causal, scale, stream)
+    return o, lse
+
+
+def backward(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None, stream=None):
+    import torch
+
+    B, Nq, Hq, d = q.shape
+    ws = torch.empty(fa_bwd_workspace_size(B, Hq, Nq, d), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, causal, scale, stream)
+    return dq, dk, dv
+
+
+def decode(q, k_cache, v_cache, seqlens, scale: float | None = None, stream=None):
+    import torch
+
+    B, _, Hq, d = q.shape
+    ws = torch.empty(fa_decode_workspace_size(B, Hq, k_cache.shape[1], d), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    fa_decode(q, k_cache, v_cache, seqlens, o, lse, ws, scale, stream)
+    return o, lse
+
+
+# ---- planner helpers -----------------------------------------------------------------------
+
+def wave_efficiency(n_blocks: int, n_cus: int) -> float:
+    return float(lib().fa_wave_efficiency(n_blocks, n_cus))
+
+
+def plan_splits(n_blocks: int, n_cus: int, frac: float = 0.85) -> int:
+    return int(lib().fa_plan_splits(n_blocks, n_cus, frac))
+
+
+def schedule_makespan(tasks, workers: int, longest_first: bool):
+    n = len(tasks)
+    arr = (ctypes.c_int * max(n, 1))(*tasks)
+    loads = (ctypes.c_int * workers)()
+    ms = lib().fa_schedule_makespan(arr, n, workers, int(longest_first), loads)
+    return ms, list(loads)
+
+
+def causal_tiles(n: int, br: int, bc: int) -> int:
+    return int(lib().fa_causal_tiles(n, br, bc))
+
+
+def decode_chunk(B: int, Hkv: int, Nk_max: int) -> int:
+    return int(lib().fa_decode_chunk(B, Hkv, Nk_max))

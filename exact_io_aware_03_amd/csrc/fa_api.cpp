@@ -1,0 +1,206 @@
+// C ABI of libfa: argument validation, workspace layout, planning and kernel dispatch.
+// Every check runs on the host before any HIP call, so an invalid call enqueues nothing.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <numeric>
+#include <vector>
+
+#include "../../include/fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+thread_local char g_hip_msg[256] = "no HIP error recorded";
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return FA_OK;
+  std::snprintf(g_hip_msg, sizeof(g_hip_msg), "HIP error %d: %s", (int)e, hipGetErrorString(e));
+  return FA_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int common_checks(int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1) return FA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_version(void) { return FA_VERSION; }
+
+const char* fa_strerror(int code) {
+  switch (code) {
+    case FA_OK: return "success";
+    case FA_ERR_INVALID_ARG: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported head dimension, dtype or mask combination";
+    case FA_ERR_HIP: return g_hip_msg;
+    case FA_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status code";
+  }
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Nq,
+           int Nk, int d, int causal, float scale, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_INVALID_ARG;
+  int st = common_checks(B, Hq, Hkv, Nq, Nk, d, scale);
+  if (st != FA_OK) return st;
+  if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  if (causal && Nq != Nk) return FA_ERR_UNSUPPORTED;
+  fa::FwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.G = Hq / Hkv;
+  a.q_row = (long)Hq * d;
+  a.k_row = (long)Hkv * d;
+  a.c = scale * 1.4426950408889634f;
+  a.causal = causal ? 1 : 0;
+  a.n_qblk = (Nq + fa::kFwdRows - 1) / fa::kFwdRows;
+  const long tasks = (long)B * Hq * a.n_qblk;
+  if (tasks > INT_MAX) return FA_ERR_INVALID_ARG;
+  a.n_tasks = (int)tasks;
+  hipStream_t s = (hipStream_t)stream;
+  return hip_status(dtype == FA_BF16 ? fa::launch_fwd_bf16(a, d, s) : fa::launch_fwd_f32(a, d, s));
+}
+
+size_t fa_bwd_workspace_size(int B, int Hq, int Nq, int d) {
+  if (B < 1 || Hq < 1 || Nq < 1 || d < 1) return 0;
+  const size_t rows = (size_t)B * Hq * Nq;
+  return align256(rows * sizeof(float)) + rows * (size_t)d * sizeof(float);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+           void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+           int dtype, void* workspace, size_t ws_bytes, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+  for (const void* p : {q, k, v, o, dout, (const void*)lse, (const void*)dq, (const void*)dk, (const void*)dv})
+    if (!aligned16(p)) return FA_ERR_INVALID_ARG;
+  int st = common_checks(B, Hq, Hkv, Nq, Nk, d, scale);
+  if (st != FA_OK) return st;
+  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (causal && Nq != Nk) return FA_ERR_UNSUPPORTED;
+  const size_t need = fa_bwd_workspace_size(B, Hq, Nq, d);
+  if (!workspace || ws_bytes < need || !aligned16(workspace)) return FA_ERR_WORKSPACE;
+  fa::BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.dvec = (float*)workspace;
+  a.dq_acc = (float*)((char*)workspace + align256((size_t)B * Hq * Nq * sizeof(float)));
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.G = Hq / Hkv;
+  a.q_row = (long)Hq * d;
+  a.k_row = (long)Hkv * d;
+  a.scale = scale;
+  a.c = scale * 1.4426950408889634f;
+  a.causal = causal ? 1 : 0;
+  a.n_kvblk = (Nk + fa::kBwdKeys - 1) / fa::kBwdKeys;
+  const long tasks = (long)B * Hkv * a.n_kvblk;
+  if (tasks > INT_MAX || (long)B * Nq * Hq > INT_MAX / 4) return FA_ERR_INVALID_ARG;
+  a.n_tasks = (int)tasks;
+  return hip_status(fa::launch_bwd(a, d, (hipStream_t)stream));
+}
+
+int fa_decode_chunk(int B, int Hkv, int Nk_max) {
+  if (B < 1 || Hkv < 1 || Nk_max < 1) return fa::kDecMinChunk;
+  if (const char* env = std::getenv("FA_DECODE_CHUNK")) {  // sweep override, multiple of 256
+    const int c = std::atoi(env);
+    if (c >= fa::kDecMinChunk && c % fa::kDecMinChunk == 0 && c <= 8192) return c;
+  }
+  // Largest chunk that still gives at least 8192 (sequence, kv head, chunk) units, i.e. a
+  // few dozen per CU even when lengths are ragged; longer chunks cut partial traffic.
+  for (int c : {2048, 1024, 512}) {
+    const long units = (long)B * Hkv * ((Nk_max + c - 1) / c);
+    if (units >= 8192) return c;
+  }
+  return fa::kDecMinChunk;
+}
+
+size_t fa_decode_workspace_size(int B, int Hq, int Nk_max, int d) {
+  if (B < 1 || Hq < 1 || Nk_max < 1 || d < 1) return 0;
+  const size_t slots = (size_t)B * Hq * ((Nk_max + fa::kDecMinChunk - 1) / fa::kDecMinChunk);
+  return align256(slots * d * sizeof(float)) + slots * 2 * sizeof(float);
+}
+
+int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int* seqlens_k, void* o, float* lse,
+              int B, int Hq, int Hkv, int Nq, int Nk_max, int d, float scale, int dtype, void* workspace,
+              size_t ws_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !seqlens_k || !o || !lse) return FA_ERR_INVALID_ARG;
+  for (const void* p : {q, k_cache, v_cache, (const void*)o, (const void*)lse})
+    if (!aligned16(p)) return FA_ERR_INVALID_ARG;
+  if (Nq != 1) return FA_ERR_INVALID_ARG;
+  int st = common_checks(B, Hq, Hkv, 1, Nk_max, d, scale);
+  if (st != FA_OK) return st;
+  if (dtype != FA_BF16 || Hq / Hkv > 16) return FA_ERR_UNSUPPORTED;
+  const size_t need = fa_decode_workspace_size(B, Hq, Nk_max, d);
+  if (!workspace || ws_bytes < need || !aligned16(workspace)) return FA_ERR_WORKSPACE;
+  if ((long)B * Nk_max * Hkv > INT_MAX / 128) return FA_ERR_INVALID_ARG;
+  fa::DecArgs a{};
+  a.q = q; a.k = k_cache; a.v = v_cache; a.seqlens = seqlens_k; a.o = o; a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.Nk_max = Nk_max; a.d = d;
+  a.chunk = fa_decode_chunk(B, Hkv, Nk_max);
+  a.n_chunks_max = (Nk_max + fa::kDecMinChunk - 1) / fa::kDecMinChunk;
+  const size_t slots = (size_t)B * Hq * a.n_chunks_max;
+  a.part_o = (float*)workspace;
+  a.part_ml = (float*)((char*)workspace + align256(slots * d * sizeof(float)));
+  a.k_row = (long)Hkv * d;
+  a.c = scale * 1.4426950408889634f;
+  return hip_status(fa::launch_decode(a, (hipStream_t)stream));
+}
+
+// ---- planner helpers -------------------------------------------------------------------------
+
+double fa_wave_efficiency(int n_blocks, int n_cus) {
+  if (n_blocks < 1 || n_cus < 1) return 0.0;
+  const long waves = (n_blocks + (long)n_cus - 1) / n_cus;
+  return (double)n_blocks / (double)(waves * n_cus);
+}
+
+int fa_plan_splits(int n_blocks, int n_cus, double frac) {
+  if (n_blocks < 1 || n_cus < 1 || !(frac > 0.0) || frac > 1.0) return -1;
+  constexpr int kMaxSplits = 128;
+  double best = 0.0;
+  for (int s = 1; s <= kMaxSplits; ++s) best = std::max(best, fa_wave_efficiency(n_blocks * s, n_cus));
+  for (int s = 1; s <= kMaxSplits; ++s)
+    if (fa_wave_efficiency(n_blocks * s, n_cus) >= frac * best) return s;
+  return 1;
+}
+
+int fa_schedule_makespan(const int* w, int n, int workers, int longest_first, int* loads_out) {
+  if (!w || n < 0 || workers < 1) return -1;
+  std::vector<int> order(n);
+  std::iota(order.begin(), order.end(), 0);
+  if (longest_first) std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return w[x] > w[y]; });
+  std::vector<long> load(workers, 0);
+  for (int idx : order) {
+    if (w[idx] < 0) return -1;
+    const int tgt = (int)(std::min_element(load.begin(), load.end()) - load.begin());  // lowest index on ties
+    load[tgt] += w[idx];
+  }
+  if (loads_out)
+    for (int i = 0; i < workers; ++i) loads_out[i] = (int)load[i];
+  return (int)*std::max_element(load.begin(), load.end());
+}
+
+long fa_causal_tiles(int n, int br, int bc) {
+  if (n < 1 || br < 1 || bc < 1) return -1;
+  long tiles = 0;
+  for (int i = 0; i * br < n; ++i) {
+    const int last_q = std::min(n, (i + 1) * br) - 1;
+    tiles += last_q / bc + 1;
+  }
+  return tiles;
+}
+
+}  // extern "C"

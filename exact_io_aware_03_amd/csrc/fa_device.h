@@ -1,0 +1,92 @@
+// Device-side building blocks shared by the gfx950 attention kernels.
+//
+// MFMA operand conventions used throughout (CDNA3/CDNA4 32x32 and 16x16 matrix cores, wave64):
+//   v_mfma_f32_32x32x16_bf16: A is 32(M) x 16(K), B is 16(K) x 32(N). Lane l supplies row
+//     (A) or column (B) l%32 and the 8 consecutive K slots [8*(l/32), 8*(l/32)+8). The 32x32
+//     fp32 result gives lane l column l%32 and, in register i (0..15), row
+//     8*(i/4) + 4*(l/32) + i%4.
+//   v_mfma_f32_16x16x32_bf16: A is 16 x 32, B is 32 x 16. Lane l supplies row/column l%16
+//     and K slots [8*(l/16), 8*(l/16)+8). Result: lane l holds column l%16, rows
+//     4*(l/16) + i, i = 0..3.
+//   v_mfma_f32_32x32x2_f32: lane l supplies row/column l%32 and the single K slot l/32.
+// A and B always assign K slots to lanes identically, so any consistent relabelling of the
+// contraction index between the two operands leaves the product unchanged; the kernels use
+// that freedom to hand the softmax output straight from the accumulator registers to the
+// next product without a trip through LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ f32x16 mfma_32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_32x32x2f(float a, float b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 r;
+  r[0] = (__bf16)lo;
+  r[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Reductions over the two wave halves (lane l and lane l^32) with v_permlane32_swap. Each
+// of the two results holds one copy of either half's value, so max/sum of the pair is the
+// reduction in every lane.
+__device__ __forceinline__ float halves_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Hardware dispatches consecutive workgroup ids round-robin over the 8 XCDs. Give every XCD
+// one contiguous range of the task list instead, so tasks that read the same K/V rows run
+// under the same L2. Bijective for any n.
+__device__ __forceinline__ int xcd_contiguous_task(int wg, int n) {
+  constexpr int kXcd = 8;
+  const int per = n / kXcd, rem = n % kXcd;
+  const int x = wg % kXcd, i = wg / kXcd;
+  return x * per + (x < rem ? x : rem) + i;
+}
+
+// Row relabelling used for the A operand of the score product: swapping bits 2 and 3 of the
+// row index makes accumulator register i of lane half h hold contraction index
+// (i & 7) + 8*h + 16*(i >> 3), i.e. each lane half owns 8 consecutive keys per 16-key step,
+// exactly the K-slot layout the next MFMA expects.
+__device__ __forceinline__ int swap_bits23(int r) {
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+// XOR swizzle of 16-byte chunks for row-major LDS tiles read 32 rows at a time through the
+// relabelling above: the 8 rows any 8 consecutive lanes touch land in 8 distinct chunks.
+__device__ __forceinline__ int swz_perm_rows(int row) { return (row & 3) | ((row >> 1) & 4); }
+
+}  // namespace fa

@@ -1,0 +1,75 @@
+// Host-side launch interface between the C-ABI layer (fa_api.cpp) and the kernel files.
+// Everything here assumes arguments were validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, Nq, Nk, G;
+  long q_row;  // elements between consecutive positions of Q/O (Hq * d)
+  long k_row;  // elements between consecutive positions of K/V (Hkv * d)
+  float c;     // softmax scale * log2(e): scores are kept in base-2 units
+  int causal;
+  int n_qblk;   // query blocks per (batch, head)
+  int n_tasks;  // B * Hq * n_qblk
+};
+
+struct DecArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int* seqlens;
+  void* o;
+  float* lse;
+  float* part_o;   // [B, Hq, n_chunks_max, d] unnormalised partial outputs
+  float* part_ml;  // [B, Hq, n_chunks_max, 2] partial (max, sum) in base-2 units
+  int B, Hq, Hkv, G, Nk_max, d;
+  int chunk;         // keys per workgroup
+  int n_chunks_max;  // ceil(Nk_max / 256): stride of the partial arrays
+  long k_row;
+  float c;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dvec;    // D = rowsum(dO * O), [B, Hq, Nq]
+  float* dq_acc;  // fp32 dQ accumulator, [B, Nq, Hq, d]
+  int B, Hq, Hkv, Nq, Nk, G;
+  long q_row, k_row;
+  float scale;
+  float c;
+  int causal;
+  int n_kvblk;
+  int n_tasks;
+};
+
+// Planner constants shared by the host code and the kernels.
+constexpr int kFwdRows = 128;     // query rows per forward workgroup (4 waves x 32)
+constexpr int kFwdKeys = 64;      // keys per forward K/V tile
+constexpr int kFwdF32Keys = 32;   // keys per tile in the fp32 forward
+constexpr int kDecMinChunk = 256; // smallest decode chunk (4 waves x 64 keys)
+constexpr int kBwdKeys = 128;     // keys per backward workgroup (4 waves x 32)
+constexpr int kBwdRows = 64;      // query rows per backward inner step
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdArgs& a, int d, hipStream_t s);
+hipError_t launch_decode(const DecArgs& a, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t s);
+
+}  // namespace fa

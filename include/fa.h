@@ -1,0 +1,126 @@
+/*
+ * fa.h -- C ABI of the gfx950 exact-attention library (libfa.so).
+ *
+ * The library computes exact scaled-dot-product attention,
+ *     O = softmax(scale * Q K^T) V,     L_i = log sum_j exp(scale * q_i . k_j)  (natural log),
+ * tile by tile with an online softmax, so the N_q x N_k score and probability matrices never
+ * reach device memory. Sources: "Lecture 21: Optimizing Attention for Modern Hardware
+ * (FlashAttention 1-4)", CMU 11-868 notes -- §0.4 (problem and notation, L = m + log l),
+ * §2.2 (online softmax), §2.5 (causal masking), §2.6 (backward by recomputation, D =
+ * rowsum(dO * O)), §3 (query-block parallel forward), §6.1-6.2 (split-KV decode, GQA packing);
+ * "FlashAttention Tiling 策略与在线 Softmax" (ybb.press), §3 (tiled forward), §5 (backward),
+ * §7 (Flash-Decoding).
+ *
+ * Conventions shared by every entry point
+ *   Layout   Q, O, dO, dQ: [B, N_q, H_q, d] contiguous, d innermost ("BSHD").
+ *            K, V, dK, dV: [B, N_k, H_kv, d] contiguous.
+ *            lse (L) and the backward's D: fp32 [B, H_q, N_q] contiguous.
+ *   GQA      H_q must be a multiple of H_kv; query head h reads kv head h / (H_q / H_kv).
+ *   Causal   key j is visible to query i iff j <= i; requires N_q == N_k.
+ *   Scale    multiplies the raw scores before the softmax; must be finite and > 0.
+ *   dtype    FA_BF16: Q/K/V/O/dO/dQ/dK/dV are bfloat16, accumulation fp32, lse fp32.
+ *            FA_F32 : all tensors fp32 (forward only), probabilities kept in fp32.
+ *   Memory   every pointer is a device pointer owned by the caller, 16-byte aligned. The
+ *            library never allocates or frees memory and holds no state between calls;
+ *            scratch space is a caller-provided workspace sized by the *_workspace_size
+ *            queries. Calls are thread-safe.
+ *   Streams  `stream` is a hipStream_t (NULL = default stream). Work is enqueued and the
+ *            call returns; buffers must stay valid until the stream has passed it. Results
+ *            are defined once the stream is synchronised.
+ *   Errors   0 on success, a negative FA_ERR_* code otherwise. Arguments are validated on
+ *            the host before any HIP call, so an invalid call has no effect. FA_ERR_HIP
+ *            reports a launch failure (fa_strerror gives the HIP text); faults inside a
+ *            kernel surface at the caller's next synchronisation.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_VERSION 1
+
+enum fa_dtype { FA_F32 = 0, FA_BF16 = 1 };
+
+enum fa_status {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1, /* null pointer, size < 1, H_q % H_kv != 0, bad scale, misalignment */
+  FA_ERR_UNSUPPORTED = -2, /* d not in {64, 128}, dtype not supported by the call, causal with N_q != N_k */
+  FA_ERR_HIP = -3,         /* a kernel launch failed */
+  FA_ERR_WORKSPACE = -4    /* workspace pointer null or smaller than the size query returned */
+};
+
+/*
+ * Forward: O and L for Q [B,Nq,Hq,d], K/V [B,Nk,Hkv,d].
+ * Per row i: m_i = max_j s_ij, l_i = sum_j exp(s_ij - m_i), O_i = sum_j exp(s_ij - m_i) v_j / l_i,
+ * L_i = m_i + ln l_i (Lecture 21 notes §0.4, §2.2, §3.2). d in {64, 128}; dtype FA_BF16 or FA_F32.
+ * o has Q's layout and dtype; lse is fp32 [B, Hq, Nq].
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+           int Nq, int Nk, int d, int causal, float scale, int dtype, void* stream);
+
+/* Workspace bytes fa_bwd needs: D (fp32 B*Hq*Nq) and an fp32 dQ accumulator (B*Nq*Hq*d). */
+size_t fa_bwd_workspace_size(int B, int Hq, int Nq, int d);
+
+/*
+ * Backward of f = sum(O * dO) given the forward's O and lse (Lecture 21 notes §2.6):
+ * P = exp(scale*S - L) is recomputed per tile; dV = P^T dO; dP = dO V^T; dS = P * (dP - D) with
+ * D = rowsum(dO * O); dQ = scale * dS K; dK = scale * dS^T Q. For GQA, dK and dV sum over the
+ * query heads of a group. dtype FA_BF16 only (fp32 gives FA_ERR_UNSUPPORTED). dq has Q's layout,
+ * dk and dv K's. dQ is accumulated with fp32 atomics, so results may differ between runs in the
+ * last bits.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+           void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+           float scale, int dtype, void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes fa_decode needs: split-KV partials for up to ceil(Nk_max/256) splits. */
+size_t fa_decode_workspace_size(int B, int Hq, int Nk_max, int d);
+
+/*
+ * Decode: one query per sequence against a padded KV cache (Lecture 21 notes §6.1-6.2).
+ * q [B,1,Hq,d]; k_cache, v_cache [B,Nk_max,Hkv,d]; seqlens_k int32 [B] on the device: sequence b
+ * attends its first seqlens_k[b] cached keys (values are clamped to [1, Nk_max]; rows past the
+ * length are never read). The keys are split into chunks, each chunk yields a partial (m, l, o)
+ * for the H_q/H_kv query heads that share a kv head, and a second kernel merges the partials by
+ * logsumexp. Nq must be 1; dtype FA_BF16; H_q/H_kv <= 16. o [B,1,Hq,d] bf16, lse fp32 [B,Hq].
+ */
+int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int* seqlens_k, void* o,
+              float* lse, int B, int Hq, int Hkv, int Nq, int Nk_max, int d, float scale, int dtype,
+              void* workspace, size_t ws_bytes, void* stream);
+
+/* Static text for a status code (for FA_ERR_HIP: the last HIP error seen by this thread). */
+const char* fa_strerror(int code);
+int fa_version(void);
+
+/* ---- host planner helpers (pure host code; exported so the scheduling rules can be tested) ---- */
+
+/* Fraction of CU slots busy when n_blocks equal blocks run in waves over n_cus CUs
+ * (Lecture 21 notes §3.3, wave quantisation). */
+double fa_wave_efficiency(int n_blocks, int n_cus);
+
+/* Smallest split count s in [1, 128] whose wave efficiency for n_blocks*s blocks is at least
+ * frac times the best over that range (Lecture 21 notes §6.1, exercise 11). */
+int fa_plan_splits(int n_blocks, int n_cus, double frac);
+
+/* Greedy list scheduling of n task lengths onto `workers`: each task goes to the least-loaded
+ * worker (lowest index on ties), in arrival order or, with longest_first, longest task first
+ * (Lecture 21 notes §4.5, LPT). Writes the final loads to loads_out (may be NULL) and returns
+ * the makespan, or -1 on bad arguments. */
+int fa_schedule_makespan(const int* w, int n, int workers, int longest_first, int* loads_out);
+
+/* Number of (query block, key tile) pairs a causal pass computes for N_q = N_k = n with
+ * br-row query blocks and bc-key tiles, whole tiles above the diagonal skipped (§2.5). */
+long fa_causal_tiles(int n, int br, int bc);
+
+/* Keys per decode chunk the library would use for this shape (a multiple of 256). */
+int fa_decode_chunk(int B, int Hkv, int Nk_max);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

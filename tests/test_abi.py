@@ -1,0 +1,151 @@
+"""The C-ABI library loads, exports every function include/fa.h declares, and validates its
+arguments on the host (no GPU needed: every call here fails validation before any HIP call).
+The planner helpers are pinned to the numbers printed in the lecture notes."""
+
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import exact_io_aware_03_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLD = json.load(open(os.path.join(ROOT, "tests", "golden", "lecture21_pins.json")))["pins"]
+
+INVALID, UNSUPPORTED, WORKSPACE = -1, -2, -4
+P = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: validation rejects the call first
+MIS = ctypes.c_void_p(0x10008)  # misaligned
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "fa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = fa.lib()
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(fa.EXPORTED)
+    assert L.fa_version() == 1
+
+
+def fwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=64, causal=0, scale=0.125, dtype=1)
+    a.update(kw)
+    return fa.lib().fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"],
+                           a["d"], a["causal"], a["scale"], a["dtype"], None)
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(q=None), INVALID), (dict(lse=None), INVALID), (dict(o=MIS), INVALID),
+        (dict(B=0), INVALID), (dict(Nk=0), INVALID), (dict(Hq=3, Hkv=2), INVALID),
+        (dict(scale=0.0), INVALID), (dict(scale=-1.0), INVALID), (dict(scale=float("nan")), INVALID),
+        (dict(scale=float("inf")), INVALID),
+        (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(dtype=7), UNSUPPORTED),
+        (dict(causal=1, Nq=8, Nk=9), UNSUPPORTED),
+    ],
+)
+def test_fwd_validation(kw, code):
+    assert fwd(**kw) == code
+
+
+def bwd(ws=P, ws_bytes=None, **kw):
+    a = dict(B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=64, causal=0, scale=0.125, dtype=1)
+    a.update(kw)
+    need = fa.fa_bwd_workspace_size(a["B"], a["Hq"], a["Nq"], a["d"])
+    ws_bytes = need if ws_bytes is None else ws_bytes
+    ptrs = [kw.pop(n, P) for n in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv")]
+    return fa.lib().fa_bwd(*ptrs, a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["causal"], a["scale"],
+                           a["dtype"], ws, ws_bytes, None)
+
+
+def test_bwd_validation():
+    need = fa.fa_bwd_workspace_size(1, 2, 8, 64)
+    assert need >= 2 * 8 * 4 + 2 * 8 * 64 * 4
+    assert bwd(dtype=0) == UNSUPPORTED  # fp32 backward is not provided
+    assert bwd(ws=None) == WORKSPACE
+    assert bwd(ws_bytes=need - 1) == WORKSPACE
+    assert bwd(Hq=2, Hkv=3) == INVALID
+    assert bwd(causal=1, Nk=9) == UNSUPPORTED
+    assert bwd(d=32) == UNSUPPORTED
+    assert fa.lib().fa_bwd(None, P, P, P, P, P, P, P, P, 1, 2, 1, 8, 8, 64, 0, 0.1, 1, P, need, None) == INVALID
+
+
+def dec(ws=P, ws_bytes=None, **kw):
+    a = dict(B=2, Hq=8, Hkv=2, Nq=1, Nk=300, d=128, scale=0.1, dtype=1)
+    a.update(kw)
+    need = fa.fa_decode_workspace_size(a["B"], a["Hq"], a["Nk"], a["d"])
+    ws_bytes = need if ws_bytes is None else ws_bytes
+    return fa.lib().fa_decode(P, P, P, kw.get("seqlens", P), P, P, a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"],
+                              a["d"], a["scale"], a["dtype"], ws, ws_bytes, None)
+
+
+def test_decode_validation():
+    assert dec(Nq=2) == INVALID
+    assert dec(seqlens=None) == INVALID
+    assert dec(dtype=0) == UNSUPPORTED
+    assert dec(Hq=64, Hkv=2) == UNSUPPORTED  # more than 16 query heads per kv head
+    assert dec(ws=None) == WORKSPACE
+    assert dec(ws_bytes=16) == WORKSPACE
+    # partials for ceil(300/256) = 2 splits of 2*8 query heads, d + 2 floats each
+    assert fa.fa_decode_workspace_size(2, 8, 300, 128) >= 2 * 8 * 2 * (128 + 2) * 4
+
+
+def test_strerror_names_every_code():
+    for c in (0, -1, -2, -3, -4):
+        assert fa.lib().fa_strerror(c)
+    assert b"unknown" in fa.lib().fa_strerror(5)
+
+
+# ---- planner helpers pinned to the lecture's printed numbers --------------------------------
+
+def test_wave_efficiency_pin():
+    pin = GOLD["wave_efficiency_256_blocks"]
+    assert round(fa.wave_efficiency(256, 108), 2) == pin["sms_108"]
+    assert round(fa.wave_efficiency(256, 132), 2) == pin["sms_132"]
+
+
+def test_split_heuristic_pins():
+    p = GOLD["decode_splits_b1_h32_sms132"]
+    assert round(fa.wave_efficiency(p["blocks"], p["sms"]), 2) == p["no_split_util"]
+    assert fa.plan_splits(p["blocks"], p["sms"], 0.85) == p["splits"]
+    assert round(fa.wave_efficiency(p["blocks"] * p["splits"], p["sms"]), 2) == p["split_util"]
+    p = GOLD["decode_splits_b2_hkv8_sms132"]
+    assert round(fa.wave_efficiency(p["blocks"], p["sms"]), 2) == p["no_split_util"]
+    assert fa.plan_splits(p["blocks"], p["sms"], 0.85) == p["splits"]
+
+
+def test_lpt_pins():
+    p = GOLD["lpt_toy"]
+    ms, loads = fa.schedule_makespan(p["tasks"], p["workers"], longest_first=False)
+    assert loads == p["natural_loads"] and ms == max(p["natural_loads"])
+    ms, loads = fa.schedule_makespan(p["tasks"], p["workers"], longest_first=True)
+    assert loads == p["lpt_loads"] and ms == max(p["lpt_loads"])
+    p = GOLD["lpt_exercise10"]
+    assert fa.schedule_makespan(p["tasks"], p["workers"], False)[0] == p["natural_makespan"]
+    assert fa.schedule_makespan(p["tasks"], p["workers"], True)[0] == p["lpt_makespan"]
+    assert -(-sum(p["tasks"]) // p["workers"]) == p["lower_bound"]
+
+
+def test_causal_tile_count_pin():
+    p = GOLD["causal_tiles_n1024_block64"]
+    assert fa.causal_tiles(1024, 64, 64) == p["computed"]
+    # the forward's own tiling: 128-row query blocks, 64-key tiles
+    T = 2048 // 64
+    assert fa.causal_tiles(2048, 128, 64) == sum(2 * i + 2 for i in range(2048 // 128)) <= T * T
+
+
+def test_decode_chunk_plan():
+    assert fa.decode_chunk(64, 8, 8192) == 512
+    assert fa.decode_chunk(1, 8, 8192) == 256
+    for B, H, N in [(1, 1, 1), (3, 5, 77), (128, 8, 131072)]:
+        c = fa.decode_chunk(B, H, N)
+        assert c % 256 == 0 and 256 <= c <= 2048
