@@ -8,8 +8,9 @@ Recipe (the source pages measure on models and datasets that are not available; 
 tensors stand in for them at the shapes of the five workloads):
 
 * generator: ``numpy.random.Generator(PCG64(seed))``, ``standard_normal(dtype=float32)``;
-* draw order: Q, K, V, then dO (backward only), then the outlier mask (long-context only),
-  then the decode lengths;
+* draw order: Q, K, V, then dO (backward only), then the outlier mask (long-context only);
+  decode draws Q, then the valid cache rows of K sequence by sequence, then those of V, and
+  takes the lengths from a child stream ``PCG64([seed, 1])``;
 * bf16 workloads draw in fp32 and round each value to the nearest bf16 (ties to even); the
   arrays returned are fp32 holding exactly those bf16 values, so an upcast to fp64 gives the
   oracle the very numbers the GPU reads;
@@ -153,17 +154,16 @@ def make_decode_inputs(
     assert lengths.shape == (B,) and lengths.min() >= 1 and lengths.max() <= Nk_max
     kc = np.zeros((B, Nk_max, Hkv, d), dtype=np.float32)
     vc = np.zeros((B, Nk_max, Hkv, d), dtype=np.float32)
+    rnd = round_to_bf16 if dtype == BF16 else (lambda x: x)
     for b in range(B):
         n = int(lengths[b])
-        kc[b, :n] = _normal(rng, (n, Hkv, d))
+        kc[b, :n] = rnd(_normal(rng, (n, Hkv, d)))
     for b in range(B):
         n = int(lengths[b])
-        vc[b, :n] = _normal(rng, (n, Hkv, d))
-    out = {"q": q, "k": kc, "v": vc, "seqlens": lengths}
+        vc[b, :n] = rnd(_normal(rng, (n, Hkv, d)))
     if dtype == BF16:
-        for key in ("q", "k", "v"):
-            out[key] = round_to_bf16(out[key])
-    return out
+        q = round_to_bf16(q)
+    return {"q": q, "k": kc, "v": vc, "seqlens": lengths}
 
 
 def make_workload_inputs(w: Workload):
