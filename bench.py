@@ -111,6 +111,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="only the training-shape forward step")
     ap.add_argument("--reps", type=int, default=10, help="timed launches per extra workload")
+    ap.add_argument("--calib", action="store_true",
+                    help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (--gpus {args.gpus} refused)",
@@ -123,6 +125,13 @@ def main():
 
     fa.lib()  # fail loudly if the HIP library is missing
     torch.cuda.set_device(0)
+    if args.calib:
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")  # 1 GiB read, 1 GiB written
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---- the step: training-shape forward, without and with the causal mask ----
     w = workloads.WORKLOADS["fwd_bf16_b16h16n2048d128"]

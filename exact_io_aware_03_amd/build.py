@@ -27,6 +27,7 @@ COMMON = [
     "-std=c++17",
     "-fPIC",
     "-Wno-unused-result",
+    "-Werror=array-bounds",
     # keep the compiler from forming v_pk_{add,mul,fma}_f32 (host pass warns it does not know it)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]

@@ -68,7 +68,11 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   a.k_row = (long)Hkv * d;
   a.c = scale * 1.4426950408889634f;
   a.causal = causal ? 1 : 0;
-  a.n_qblk = (Nq + fa::kFwdRows - 1) / fa::kFwdRows;
+  const int rows = dtype == FA_BF16 ? fa::kFwdRows : fa::kFwdF32Rows;
+  a.n_qblk = (Nq + rows - 1) / rows;
+  // buffer-resource offsets are 32-bit: one batch of Q/O or K/V must stay below 2 GiB
+  const long esz = dtype == FA_BF16 ? 2 : 4;
+  if ((long)Nq * Hq * d * esz >= (1L << 31) || (long)Nk * Hkv * d * esz >= (1L << 31)) return FA_ERR_UNSUPPORTED;
   const long tasks = (long)B * Hq * a.n_qblk;
   if (tasks > INT_MAX) return FA_ERR_INVALID_ARG;
   a.n_tasks = (int)tasks;

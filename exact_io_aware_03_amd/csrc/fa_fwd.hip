@@ -2,112 +2,321 @@
 //
 // Method (Lecture 21 notes, CMU 11-868: §2.2 online softmax, §2.5 whole-tile causal skip,
 // §3.1 query-block-outer loop, §3.2 deferred normalisation with only L stored, §3.4 split-Q
-// across warps; "FlashAttention Tiling 策略与在线 Softmax", §3 tiling): one workgroup owns 128
-// query rows, each of its four waves 32 of them; K/V tiles of 64 keys stream through LDS
-// while the running max m, running sum l and the output accumulator stay in registers, so
-// the N x N scores never leave the chip.
+// across warps, §4.3 overlap of the softmax with the matrix products; "FlashAttention Tiling
+// 策略与在线 Softmax", §3 tiling): one workgroup owns 256 query rows, each of its four waves 64 of
+// them; K/V tiles of 64 keys stream through LDS while the running max m, running sum l and the
+// output accumulator stay in registers, so the N x N scores never leave the chip.
 //
 // gfx950 mapping:
-//  * scores are computed transposed, S^T = K Q^T, so every lane owns one query: the row max
-//    and row sum are in-lane reductions plus one v_permlane32_swap between the wave halves,
-//    and the rescale factor alpha is a per-lane scalar;
+//  * scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16), so every lane
+//    owns one query per 32-row block: the row max and sum are in-lane reductions plus one
+//    v_permlane32_swap, and the rescale factor alpha is a per-lane scalar;
 //  * the K rows fed to the score MFMA are relabelled (bits 2 and 3 of the row swapped), which
 //    leaves each lane half holding 8 consecutive keys per 16-key step: the probabilities go
 //    from the score accumulator straight into the B operand of O^T += V^T P^T, no LDS trip;
-//  * V is transposed once while it is written to LDS, so the A operand of the output MFMA is
-//    one ds_read_b128 per lane; K and V^T tiles use XOR-swizzled 16-byte chunks so the 8
-//    rows read by 8 neighbouring lanes fall in distinct banks;
-//  * two LDS buffers: the global loads of tile j+2 are in flight while tile j is computed,
-//    one barrier per tile;
-//  * scores stay in base-2 units (scale * log2 e folded into one FMA before v_exp_f32);
-//  * the rescale of the output accumulator is skipped when no row maximum moved;
-//  * causal: tiles wholly above a wave's rows are skipped, diagonal tiles are masked from
-//    global indices, and query blocks are scheduled longest-first inside XCD-contiguous task
-//    ranges.
+//  * 64 rows per wave: every K/V fragment read from LDS feeds two MFMAs;
+//  * software pipeline inside the wave: the score MFMAs of tile j+1 are issued while the VALU
+//    runs the softmax of tile j, and the P V MFMAs of tile j while the row sums, the bf16
+//    packing and the LDS stores of tile j+2 run; independent MFMA and VALU work from one wave
+//    overlaps on CDNA;
+//  * V is transposed in registers on its way into LDS, so the V^T operand is one ds_read_b128
+//    per lane; K and V^T tiles use XOR-swizzled 16-byte chunks (8 rows read by 8 neighbouring
+//    lanes fall in distinct banks); three LDS buffers, one barrier per tile, global loads two
+//    tiles ahead;
+//  * K/V/Q/O go through buffer instructions whose resource ends at the last valid row, so
+//    rows past N read as zero and stores past N are dropped, without per-lane branches;
+//  * scores stay in base-2 units (scale * log2 e folded into one FMA before v_exp_f32); the
+//    rescale of the output accumulator is skipped when no row maximum moved;
+//  * causal: tiles wholly above a wave's rows are skipped, diagonal tiles are masked from global
+//    indices, query blocks are scheduled longest-first inside XCD-contiguous task ranges.
 #include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int BR = kFwdRows;
-constexpr int BC = kFwdKeys;
+constexpr int kWaves = 8;                // waves per workgroup, two per SIMD
+constexpr int kThreads = 64 * kWaves;
+constexpr int QH = 1;                    // 32-row query blocks per wave
+constexpr int BR = kFwdRows;             // 256 query rows per workgroup
+constexpr int BC = kFwdKeys;             // 64 keys per tile
+constexpr int NBUF = 4;                  // LDS tile buffers: tiles j..j+3 resident or in flight
+constexpr float kTau = 8.f;              // rescale threshold, base-2 units (a factor of 256)
+static_assert(BR == 32 * QH * kWaves, "rows per workgroup");
+constexpr int kF32Threads = 256;
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void lds_t;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 template <int D>
 struct Tile {
-  static constexpr int KCH = D / 8;                        // 16-byte chunks per K row
-  static constexpr int K_BYTES = BC * D * 2;               // K tile, row-major [key][d]
-  static constexpr int V_BYTES = D * BC * 2;               // V^T tile, [d][key]
-  static constexpr int BUF = K_BYTES + V_BYTES;
-  static constexpr int K_ROWS_PER_PASS = kThreads / KCH;
-  static constexpr int K_PASSES = BC / K_ROWS_PER_PASS;    // 16-byte K loads per thread
-  static constexpr int V_BLOCKS = (BC / 4) * KCH;          // 4-key x 8-d blocks per tile
-  static_assert(V_BLOCKS <= kThreads, "one V block per thread at most");
+  static constexpr int KCH = D / 8;                 // 16-byte chunks per row
+  static constexpr int ROW = D * 2;                 // bytes per K or V row
+  static constexpr int K_BYTES = BC * ROW;          // K tile, row-major [key][d]
+  static constexpr int BUF = 2 * K_BYTES;           // K tile then V tile (both row-major)
+  static constexpr int RR = 1024 / ROW;             // rows one wave-wide 16-byte DMA covers
+  static constexpr int DMA = K_BYTES / 1024 / kWaves;  // DMA instructions per wave per tensor per tile
+  static constexpr int VMCNT = 2 * DMA;             // DMA instructions per thread per tile
 };
 
-// Swizzle of the V^T tile: row d keeps its 8 chunks (8 keys each) XOR-permuted by
-// (d ^ d>>3) & 7, distinct across both the 8 consecutive rows a read touches and the 8 rows
-// one transposing write touches.
-__device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
-
+// Chunk swizzle of the V tile, read through ds_read_b64_tr_b16 (16 lanes take a 4-row x
+// 32-byte block, the wave half 4 rows x 64 bytes): XOR-ing chunk bits 2-3 with the row's
+// position among 4 consecutive rows (d=128) or among 4 rows at 128-byte pitch (d=64) spreads
+// the 16 chunks of a wave half over 16 distinct bank groups.
 template <int D>
-__device__ __forceinline__ void load_tile(const uint16_t* kp, const uint16_t* vp, long k_row, int kv0,
-                                          int nk, u32x4 (&kst)[Tile<D>::K_PASSES], u32x4 (&vst)[4]) {
-  using T = Tile<D>;
-  const int t = threadIdx.x;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
+__device__ __forceinline__ int v_swz(int row) {
+  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
+
+// Chunk swizzle of the K tile, read 32 rows at a time through the row relabelling: the LDS
+// serves 16 lanes of a ds_read_b128 together, so the 16 rows those lanes touch must land in 16
+// distinct 16-byte bank groups -- XOR with the row's low 4 bits (d=128, 16 chunks per row) or
+// with bits 1-3 (d=64, two 128-byte rows per 256-byte bank line).
+template <int D>
+__device__ __forceinline__ int k_swz(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+
+// Raw buffer resource covering `bytes` from `base` (out-of-range loads return 0, out-of-range
+// stores are dropped). Word 3 selects 32-bit untyped access.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, long bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes >= 0x7fffffffL ? 0x7fffffff : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+}
+
+// Per-lane global byte offsets of the direct-to-LDS loads of one tile: the instruction p of
+// wave w fills 1 KiB of LDS (region kWaves*p+w), lane i landing on row RR*region + i/KCH,
+// physical chunk i%KCH; it fetches the logical chunk that the swizzle puts there.
+template <int D>
+struct TileDma {
+  int k_off[Tile<D>::DMA];
+  int v_off[Tile<D>::DMA];
+  __device__ void init(long k_row) {
+    using T = Tile<D>;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-  for (int p = 0; p < T::K_PASSES; ++p) {
-    const int key = kv0 + t / T::KCH + p * T::K_ROWS_PER_PASS;
-    kst[p] = key < nk ? *(const u32x4*)(kp + (long)key * k_row + (t % T::KCH) * 8) : zero;
+    for (int p = 0; p < T::DMA; ++p) {
+      const int row = T::RR * (kWaves * p + w) + lane / T::KCH;
+      const int pc = lane % T::KCH;
+      k_off[p] = (int)((row * k_row + (pc ^ k_swz<D>(row)) * 8) * 2);
+      v_off[p] = (int)((row * k_row + (pc ^ v_swz<D>(row)) * 8) * 2);
+    }
   }
-  if (t < T::V_BLOCKS) {
-    const int kg = t / T::KCH, dc = t % T::KCH;
+};
+
+// One wave-wide 16-byte direct-to-LDS load (non-template wrapper: the host pass of a template
+// instantiation cannot see the target builtin).
+__device__ __forceinline__ void lds_dma16(rsrc_t r, char* dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t*)dst, 16, voff, 0, 0, 0);
+}
+
+// Issue the direct-to-LDS loads of the tile starting at key kv0 into `buf`; keys at or past
+// nk land as zero. Completion is tracked by vmcnt (Tile::VMCNT instructions per thread).
+template <int D>
+__device__ __forceinline__ void dma_tile(char* buf, const uint16_t* kp, const uint16_t* vp, long k_row, int kv0,
+                                         int nk, const TileDma<D>& dm) {
+  using T = Tile<D>;
+  const long valid = ((long)(nk - 1 - kv0) * k_row + D) * 2;  // bytes up to the end of the last row
+  const rsrc_t rk = make_rsrc(kp + (long)kv0 * k_row, valid);
+  const rsrc_t rv = make_rsrc(vp + (long)kv0 * k_row, valid);
+  const int w = threadIdx.x >> 6;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = kv0 + 4 * kg + r;
-      vst[r] = key < nk ? *(const u32x4*)(vp + (long)key * k_row + dc * 8) : zero;
+  for (int p = 0; p < T::DMA; ++p) {
+    const int region = (kWaves * p + w) * 1024;
+    lds_dma16(rk, buf + region, dm.k_off[p]);
+    lds_dma16(rv, buf + T::K_BYTES + region, dm.v_off[p]);
+  }
+}
+
+// vmcnt-only wait (expcnt and lgkmcnt left unconstrained), then the workgroup barrier. Used
+// instead of __syncthreads so the direct-to-LDS loads of later tiles stay in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  __builtin_amdgcn_s_barrier();
+}
+
+__device__ __forceinline__ void zero16(f32x16& x) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = 0.f;
+}
+
+// Scores of this wave's rows against the 64 keys of one LDS tile: s[qh][kb] = K_kb Q_qh^T.
+template <int D>
+__device__ __forceinline__ void scores(const char* kt, int krow0, int h, const bf16x8 (&qf)[QH][D / 16],
+                                       f32x16 (&s)[QH][2]) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int row = 32 * kb + krow0;
+    const char* kr = kt + row * (D * 2);
+    const int sw = k_swz<D>(row);
+#pragma unroll
+    for (int qh = 0; qh < QH; ++qh) zero16(s[qh][kb]);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const bf16x8 kf = *(const bf16x8*)(kr + (((2 * ks + h) ^ sw) << 4));
+#pragma unroll
+      for (int qh = 0; qh < QH; ++qh) s[qh][kb] = mfma_32x32x16(kf, qf[qh][ks], s[qh][kb]);
     }
   }
 }
 
-template <int D>
-__device__ __forceinline__ void store_tile(char* buf, const u32x4 (&kst)[Tile<D>::K_PASSES],
-                                           const u32x4 (&vst)[4]) {
-  using T = Tile<D>;
-  const int t = threadIdx.x;
+// Register i of s[qh][kb] holds key kv0 + 32kb + (i&7) + 8h + 16(i>>3) for query q0 + 32qh + l32.
+template <bool CAUSAL>
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[QH][2], int kv0, int nk, int q0, int l32, int h) {
 #pragma unroll
-  for (int p = 0; p < T::K_PASSES; ++p) {
-    const int row = t / T::KCH + p * T::K_ROWS_PER_PASS;
-    const int ch = t % T::KCH;
-    *(u32x4*)(buf + row * (D * 2) + ((ch ^ swz_perm_rows(row)) << 4)) = kst[p];
-  }
-  if (t < T::V_BLOCKS) {
-    // Transpose the 4 keys x 8 dims block in registers: one 8-byte write per dimension.
-    const int kg = t / T::KCH, dc = t % T::KCH;
-    char* vt = buf + T::K_BYTES;
+  for (int qh = 0; qh < QH; ++qh)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int d = dc * 8 + i;
-      const uint32_t w0 = vst[0][i >> 1], w1 = vst[1][i >> 1], w2 = vst[2][i >> 1], w3 = vst[3][i >> 1];
-      u32x2 out;
-      if (i & 1) {
-        out[0] = (w0 >> 16) | (w1 & 0xffff0000u);
-        out[1] = (w2 >> 16) | (w3 & 0xffff0000u);
-      } else {
-        out[0] = (w0 & 0xffffu) | (w1 << 16);
-        out[1] = (w2 & 0xffffu) | (w3 << 16);
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kv0 + 32 * kb + (i & 7) + 8 * h + 16 * (i >> 3);
+        if (key >= nk || (CAUSAL && key > q0 + 32 * qh + l32)) s[qh][kb][i] = kNegInf;
       }
-      *(u32x2*)(vt + d * (BC * 2) + (((kg >> 1) ^ vt_swz(d)) << 4) + ((kg & 1) << 3)) = out;
+}
+
+__device__ __forceinline__ float max32(const f32x16& a, const f32x16& b) {
+  float m0 = fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
+  float m1 = fmaxf(fmaxf(a[4], a[5]), fmaxf(a[6], a[7]));
+  float m2 = fmaxf(fmaxf(a[8], a[9]), fmaxf(a[10], a[11]));
+  float m3 = fmaxf(fmaxf(a[12], a[13]), fmaxf(a[14], a[15]));
+  float m4 = fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3]));
+  float m5 = fmaxf(fmaxf(b[4], b[5]), fmaxf(b[6], b[7]));
+  float m6 = fmaxf(fmaxf(b[8], b[9]), fmaxf(b[10], b[11]));
+  float m7 = fmaxf(fmaxf(b[12], b[13]), fmaxf(b[14], b[15]));
+  return fmaxf(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)), fmaxf(fmaxf(m4, m5), fmaxf(m6, m7)));
+}
+
+__device__ __forceinline__ float sum32(const f32x16& a, const f32x16& b) {
+  float s0 = (a[0] + a[1]) + (a[2] + a[3]), s1 = (a[4] + a[5]) + (a[6] + a[7]);
+  float s2 = (a[8] + a[9]) + (a[10] + a[11]), s3 = (a[12] + a[13]) + (a[14] + a[15]);
+  float s4 = (b[0] + b[1]) + (b[2] + b[3]), s5 = (b[4] + b[5]) + (b[6] + b[7]);
+  float s6 = (b[8] + b[9]) + (b[10] + b[11]), s7 = (b[12] + b[13]) + (b[14] + b[15]);
+  return ((s0 + s1) + (s2 + s3)) + ((s4 + s5) + (s6 + s7));
+}
+
+// A operand of O^T += V^T P^T for d-block db and 16-key step ks, read from the row-major V tile
+// with two ds_read_b64_tr_b16: in each 16-lane group, source lane s points at row r0 + s/4,
+// columns c0 + 4(s%4) .. +3, and result lane i receives column c0 + i of rows r0 .. r0+3. With
+// r0 = 16ks + 8h + 4rd and c0 = 32db + 16((lane/16)%2), lane l ends up with column 32db + l%32
+// and keys 16ks + 8h + 0..7 -- the same K-slot order the probabilities have in the B operand.
+template <int D>
+__device__ __forceinline__ bf16x8 v_frag(const char* vt, int ks, int db, int lane) {
+  using T = Tile<D>;
+  const int s = lane & 15, g = lane >> 4;
+  i16x4 r[2];
+#pragma unroll
+  for (int rd = 0; rd < 2; ++rd) {
+    const int row = 16 * ks + 8 * (g >> 1) + 4 * rd + (s >> 2);
+    const int col_b = (32 * db + 16 * (g & 1) + 4 * (s & 3)) * 2;  // byte column
+    const int off = row * T::ROW + (((col_b >> 4) ^ v_swz<D>(row)) << 4) + (col_b & 15);
+    r[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + off));
+  }
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 c = __builtin_shufflevector(r[0], r[1], 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
+}
+
+// One K/V tile of the pipelined loop for this wave's rows. On entry s holds the raw scores
+// of tile j; with NEXT, the scores of tile j+1 are produced into s on exit.
+template <int D, bool CAUSAL, bool NEXT>
+__device__ __forceinline__ void tile_step(char* smem, int j, const uint16_t* kp, const uint16_t* vp, long k_row,
+                                          int nk_load, int nk, const TileDma<D>& dm, int q0, int l32, int h, int lane,
+                                          int krow0, float c, const bf16x8 (&qf)[QH][D / 16], f32x16 (&s)[QH][2],
+                                          f32x16 (&o)[QH][D / 32], float (&m)[QH], float (&l)[QH]) {
+  using T = Tile<D>;
+  const int kv0 = j * BC;
+  const char* cur = smem + (j % NBUF) * T::BUF;
+  // buffer (j+3)%4 held tile j-1, released by the barrier that ended iteration j-1
+  dma_tile<D>(smem + ((j + 3) % NBUF) * T::BUF, kp, vp, k_row, (j + 3) * BC, nk_load, dm);
+  if (kv0 + BC > nk || (CAUSAL && kv0 + BC - 1 > q0)) mask_tile<CAUSAL>(s, kv0, nk, q0, l32, h);
+
+  // ---- phase A: scores of tile j+1 (MFMA) interleaved with the softmax of tile j (VALU) ----
+  f32x16 sn[QH][2];
+  if (NEXT) scores<D>(smem + ((j + 1) % NBUF) * T::BUF, krow0, h, qf, sn);
+  // Conditional rescaling (Lecture 21 notes §5.3): the reference m only moves when the tile's
+  // max exceeds it by more than kTau (base 2), so most tiles skip the O rescale; exponents stay
+  // <= kTau and the reference cancels in O = acc / l and in L = m + log2 l.
+  float alpha[QH];
+  bool moved = false;
+#pragma unroll
+  for (int qh = 0; qh < QH; ++qh) {
+    const float mx = halves_max(max32(s[qh][0], s[qh][1])) * c;
+    const bool up = mx > m[qh] + kTau;
+    const float m_new = up ? mx : m[qh];
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    alpha[qh] = up ? fast_exp2(m[qh] - m_use) : 1.f;
+    moved |= up;
+    m[qh] = m_new;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[qh][kb][i] = fast_exp2(fmaf(s[qh][kb][i], c, -m_use));
+  }
+  if (NEXT) {
+#pragma unroll
+    for (int g = 0; g < 2 * (D / 16); ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one K fragment read
+      __builtin_amdgcn_sched_group_barrier(0x008, QH, 0);  // its MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // a slice of the softmax
     }
+  }
+  if (__ballot(moved)) {
+#pragma unroll
+    for (int qh = 0; qh < QH; ++qh)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[qh][db][i] *= alpha[qh];
+  }
+
+  // ---- phase B: O^T += V^T P^T (MFMA) interleaved with packing and the row sums (VALU) ----
+#pragma unroll
+  for (int ks = 0; ks < BC / 16; ++ks) {
+    bf16x8 pf[QH];
+#pragma unroll
+    for (int qh = 0; qh < QH; ++qh) {
+      const f32x16& sv = s[qh][ks >> 1];
+      const int e = (ks & 1) * 8;
+      u32x4 pw;
+      pw[0] = pack_bf16x2(sv[e + 0], sv[e + 1]);
+      pw[1] = pack_bf16x2(sv[e + 2], sv[e + 3]);
+      pw[2] = pack_bf16x2(sv[e + 4], sv[e + 5]);
+      pw[3] = pack_bf16x2(sv[e + 6], sv[e + 7]);
+      pf[qh] = as_bf16x8(pw);
+    }
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const bf16x8 vf = v_frag<D>(cur + T::K_BYTES, ks, db, lane);
+#pragma unroll
+      for (int qh = 0; qh < QH; ++qh) o[qh][db] = mfma_32x32x16(vf, pf[qh], o[qh][db]);
+    }
+  }
+#pragma unroll
+  for (int qh = 0; qh < QH; ++qh) l[qh] = l[qh] * alpha[qh] + sum32(s[qh][0], s[qh][1]);
+#pragma unroll
+  for (int g = 0; g < (BC / 16) * (D / 32); ++g) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two transposed V reads
+    __builtin_amdgcn_sched_group_barrier(0x008, QH, 0);  // their MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // packing / row sums
+  }
+
+  wait_vm_barrier<T::VMCNT>();  // tile j+2 landed; tile j+3 may still be in flight
+  if (NEXT) {
+#pragma unroll
+    for (int qh = 0; qh < QH; ++qh)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[qh][kb] = sn[qh][kb];
   }
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   using T = Tile<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * T::BUF];
+  __shared__ __attribute__((aligned(16))) char smem[NBUF * T::BUF];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5, l32 = lane & 31;
@@ -119,137 +328,88 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   const uint16_t* qp = (const uint16_t*)a.q + (long)b * a.Nq * a.q_row + hq * D;
   const uint16_t* kp = (const uint16_t*)a.k + (long)b * a.Nk * a.k_row + hk * D;
   const uint16_t* vp = (const uint16_t*)a.v + (long)b * a.Nk * a.k_row + hk * D;
+  const long q_valid = ((long)(a.Nq - 1) * a.q_row + D) * 2;
 
-  const int q0 = qb * BR + wave * 32;  // first query row of this wave
-  const int qi = q0 + l32;             // the query this lane owns
+  const int q0 = qb * BR + wave * 32 * QH;  // first query row of this wave
 
-  // Q as the B operand of S^T = K Q^T: lane holds column qi, dims [16ks + 8h, +8).
-  bf16x8 qf[D / 16];
+  // Q as the B operand of S^T = K Q^T: lane holds column q0 + 32qh + l32, dims [16ks + 8h, +8).
+  bf16x8 qf[QH][D / 16];
   {
-    const u32x4 zero = {0u, 0u, 0u, 0u};
+    const rsrc_t rq = make_rsrc(qp, q_valid);
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-      qf[ks] = as_bf16x8(qi < a.Nq ? *(const u32x4*)(qp + (long)qi * a.q_row + ks * 16 + h * 8) : zero);
+    for (int qh = 0; qh < QH; ++qh)
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks)
+        qf[qh][ks] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(
+            rq, (int)(((long)(q0 + 32 * qh + l32) * a.q_row + ks * 16 + h * 8) * 2), 0, 0));
   }
 
   int n_tiles = (a.Nk + BC - 1) / BC;
+  int last_w = n_tiles - 1;  // last tile this wave computes
   if (CAUSAL) {
-    const int last_q = min(a.Nq, (qb + 1) * BR) - 1;
-    n_tiles = min(n_tiles, last_q / BC + 1);
+    n_tiles = min(n_tiles, (min(a.Nq, (qb + 1) * BR) - 1) / BC + 1);
+    last_w = min(n_tiles - 1, (q0 + 32 * QH - 1) / BC);
+  }
+  // prefetches past the workgroup's last tile resolve to an empty buffer range (zeros, no
+  // memory traffic) so every iteration issues the same number of loads
+  const int nk_load = min(a.Nk, n_tiles * BC);
+
+  f32x16 o[QH][D / 32];
+#pragma unroll
+  for (int qh = 0; qh < QH; ++qh)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) zero16(o[qh][db]);
+  float m[QH], l[QH];
+#pragma unroll
+  for (int qh = 0; qh < QH; ++qh) {
+    m[qh] = kNegInf;
+    l[qh] = 0.f;
   }
 
-  f32x16 o[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-  float m = kNegInf, l = 0.f;
-
-  u32x4 kst[T::K_PASSES], vst[4];
-  load_tile<D>(kp, vp, a.k_row, 0, a.Nk, kst, vst);
-  store_tile<D>(smem, kst, vst);
-  if (n_tiles > 1) load_tile<D>(kp, vp, a.k_row, BC, a.Nk, kst, vst);
-  __syncthreads();
+  // tiles 0, 1, 2 in flight; wait for 0 and 1 (the last tile's loads may stay outstanding)
+  TileDma<D> dm;
+  dm.init(a.k_row);
+  dma_tile<D>(smem, kp, vp, a.k_row, 0, nk_load, dm);
+  dma_tile<D>(smem + T::BUF, kp, vp, a.k_row, BC, nk_load, dm);
+  dma_tile<D>(smem + 2 * T::BUF, kp, vp, a.k_row, 2 * BC, nk_load, dm);
+  wait_vm_barrier<T::VMCNT>();
 
   const int krow0 = swap_bits23(l32);
-  for (int j = 0; j < n_tiles; ++j) {
-    const char* cur = smem + (j & 1) * T::BUF;
-    const int kv0 = j * BC;
-    if (!CAUSAL || kv0 <= q0 + 31) {
-      // ---- scores S^T = K Q^T for 64 keys (two 32-key MFMA blocks) ----
-      f32x16 s[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-        const int row = 32 * kb + krow0;
-        const char* kr = cur + row * (D * 2);
-        const int sw = swz_perm_rows(row);
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const bf16x8 kf = *(const bf16x8*)(kr + (((2 * ks + h) ^ sw) << 4));
-          s[kb] = mfma_32x32x16(kf, qf[ks], s[kb]);
-        }
-      }
-      // register i of block kb holds key kv0 + 32kb + (i&7) + 8h + 16(i>>3)
-      if (kv0 + BC > a.Nk || (CAUSAL && kv0 + BC - 1 > q0)) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kv0 + 32 * kb + (i & 7) + 8 * h + 16 * (i >> 3);
-            if (key >= a.Nk || (CAUSAL && key > qi)) s[kb][i] = kNegInf;
-          }
-      }
-      // ---- online softmax (base 2) ----
-      float mx = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-      mx = halves_max(mx);
-      const float m_new = fmaxf(m, mx * a.c);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = fast_exp2(m - m_use);
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(fmaf(s[kb][i], a.c, -m_use));
-          s[kb][i] = p;
-          rs += p;
-        }
-      l = l * alpha + rs;  // per-half partial sum; the halves are added once at the end
-      m = m_new;
-      if (__ballot(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-      }
-      // ---- O^T += V^T P^T, 16 keys per step ----
-#pragma unroll
-      for (int ks = 0; ks < BC / 16; ++ks) {
-        const f32x16& sv = s[ks >> 1];
-        const int e = (ks & 1) * 8;
-        u32x4 pw;
-        pw[0] = pack_bf16x2(sv[e + 0], sv[e + 1]);
-        pw[1] = pack_bf16x2(sv[e + 2], sv[e + 3]);
-        pw[2] = pack_bf16x2(sv[e + 4], sv[e + 5]);
-        pw[3] = pack_bf16x2(sv[e + 6], sv[e + 7]);
-        const bf16x8 pf = as_bf16x8(pw);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const int d = 32 * db + l32;
-          const bf16x8 vf =
-              *(const bf16x8*)(cur + T::K_BYTES + d * (BC * 2) + (((2 * ks + h) ^ vt_swz(d)) << 4));
-          o[db] = mfma_32x32x16(vf, pf, o[db]);
-        }
-      }
-    }
-    if (j + 1 < n_tiles) {
-      store_tile<D>(smem + ((j + 1) & 1) * T::BUF, kst, vst);
-      if (j + 2 < n_tiles) load_tile<D>(kp, vp, a.k_row, (j + 2) * BC, a.Nk, kst, vst);
-    }
-    __syncthreads();
-  }
+  f32x16 s[QH][2];
+  scores<D>(smem, krow0, h, qf, s);
 
-  // ---- epilogue: O = acc / l, L = (m + log2 l) ln 2 ----
-  l = halves_sum(l);
-  if (qi < a.Nq) {
-    const float inv = 1.f / l;
-    uint16_t* op = (uint16_t*)a.o + ((long)b * a.Nq + qi) * a.q_row + hq * D;
+  int j = 0;
+  for (; j < last_w; ++j)
+    tile_step<D, CAUSAL, true>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, a.c, qf, s, o, m,
+                               l);
+  tile_step<D, CAUSAL, false>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, a.c, qf, s, o, m,
+                              l);
+  ++j;
+  // tiles past this wave's diagonal: keep the workgroup's barrier count
+  for (; j < n_tiles; ++j) {
+    dma_tile<D>(smem + ((j + 3) % NBUF) * T::BUF, kp, vp, a.k_row, (j + 3) * BC, nk_load, dm);
+    wait_vm_barrier<T::VMCNT>();
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // drain the tail prefetches before the workgroup ends
+
+  // ---- epilogue: O = acc / l, L = (m + log2 l) ln 2; stores past N are dropped ----
+  const rsrc_t ro = make_rsrc((uint16_t*)a.o + (long)b * a.Nq * a.q_row + hq * D, q_valid);
+#pragma unroll
+  for (int qh = 0; qh < QH; ++qh) {
+    const float lt = halves_sum(l[qh]);
+    const float inv = 1.f / lt;
+    const int qi = q0 + 32 * qh + l32;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         u32x2 w;
-        w[0] = pack_bf16x2(o[db][4 * jj + 0] * inv, o[db][4 * jj + 1] * inv);
-        w[1] = pack_bf16x2(o[db][4 * jj + 2] * inv, o[db][4 * jj + 3] * inv);
-        *(u32x2*)(op + 32 * db + 8 * jj + 4 * h) = w;
+        w[0] = pack_bf16x2(o[qh][db][4 * jj + 0] * inv, o[qh][db][4 * jj + 1] * inv);
+        w[1] = pack_bf16x2(o[qh][db][4 * jj + 2] * inv, o[qh][db][4 * jj + 3] * inv);
+        __builtin_amdgcn_raw_buffer_store_b64(
+            w, ro, (int)(((long)qi * a.q_row + 32 * db + 8 * jj + 4 * h) * 2), 0, 0);
       }
-    if (h == 0) a.lse[((long)b * a.Hq + hq) * a.Nq + qi] = (m + __log2f(l)) * kLn2;
+    if (h == 0 && qi < a.Nq) a.lse[((long)b * a.Hq + hq) * a.Nq + qi] = (m[qh] + __log2f(lt)) * kLn2;
   }
 }
 
@@ -258,7 +418,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 // probabilities kept in fp32, since rounding P to 16 bits would cost ~1e-3 of accuracy
 // (Lecture 21 notes, §5.2: bf16 P gives ~3e-3 error at N=512 vs ~3e-6 in fp32).
 template <int D>
-__global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(FwdArgs a) {
   constexpr int BK = kFwdF32Keys;
   __shared__ float k_lds[BK][D + 1];  // padded: 32 rows read column-wise, conflict free
   __shared__ float v_lds[BK][D];
@@ -272,7 +432,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
   const float* qp = (const float*)a.q + (long)b * a.Nq * a.q_row + hq * D;
   const float* kp = (const float*)a.k + (long)b * a.Nk * a.k_row + hk * D;
   const float* vp = (const float*)a.v + (long)b * a.Nk * a.k_row + hk * D;
-  const int q0 = qb * BR + wave * 32;
+  const int q0 = qb * kFwdF32Rows + wave * 32;
   const int qi = q0 + l32;
 
   float qf[D / 2];  // B operand of S^T = K Q^T: column qi, dim 2ks + h
@@ -280,7 +440,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
   for (int ks = 0; ks < D / 2; ++ks) qf[ks] = qi < a.Nq ? qp[(long)qi * a.q_row + 2 * ks + h] : 0.f;
 
   int n_tiles = (a.Nk + BK - 1) / BK;
-  if (a.causal) n_tiles = min(n_tiles, (min(a.Nq, (qb + 1) * BR) - 1) / BK + 1);
+  if (a.causal) n_tiles = min(n_tiles, (min(a.Nq, (qb + 1) * kFwdF32Rows) - 1) / BK + 1);
 
   f32x16 o[D / 32];
 #pragma unroll
@@ -292,7 +452,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
   for (int j = 0; j < n_tiles; ++j) {
     const int kv0 = j * BK;
     __syncthreads();
-    for (int e = threadIdx.x; e < BK * D; e += kThreads) {
+    for (int e = threadIdx.x; e < BK * D; e += kF32Threads) {
       const int r = e / D, c = e % D;
       const bool ok = kv0 + r < a.Nk;
       k_lds[r][c] = ok ? kp[(long)(kv0 + r) * a.k_row + c] : 0.f;
@@ -370,7 +530,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t s) {
 }
 
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, hipStream_t s) {
-  const dim3 grid(a.n_tasks), block(kThreads);
+  const dim3 grid(a.n_tasks), block(kF32Threads);
   if (d == 128) hipLaunchKernelGGL((fwd_f32_kernel<128>), grid, block, 0, s, a);
   else hipLaunchKernelGGL((fwd_f32_kernel<64>), grid, block, 0, s, a);
   return hipGetLastError();

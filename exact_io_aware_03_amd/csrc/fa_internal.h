@@ -60,7 +60,8 @@ struct BwdArgs {
 };
 
 // Planner constants shared by the host code and the kernels.
-constexpr int kFwdRows = 128;     // query rows per forward workgroup (4 waves x 32)
+constexpr int kFwdRows = 256;     // query rows per bf16 forward workgroup (4 waves x 64)
+constexpr int kFwdF32Rows = 128;  // query rows per fp32 forward workgroup (4 waves x 32)
 constexpr int kFwdKeys = 64;      // keys per forward K/V tile
 constexpr int kFwdF32Keys = 32;   // keys per tile in the fp32 forward
 constexpr int kDecMinChunk = 256; // smallest decode chunk (4 waves x 64 keys)
