@@ -8,12 +8,15 @@
 //
 // gfx950 mapping: one workgroup = (sequence b, kv head, chunk of `chunk` keys); the grid
 // covers the padded maximum length and chunks past a sequence's length exit at once, so the
-// ragged lengths stay on the device. Each wave streams 64 keys per step with 16-byte loads
-// (32 loads in flight per lane), computes S^T = K Q^T for the packed query heads with
-// v_mfma_f32_16x16x32_bf16 (query heads as the 16 MFMA columns), does the online softmax
-// on the VALU, and accumulates P V on the VALU with each lane owning 8 head dims of one key
-// in four. The four waves merge in LDS and write one fp32 partial per (query head, chunk);
-// the combine kernel merges the partials of each (sequence, query head).
+// ragged lengths stay on the device. The four waves take the chunk's 64-key steps in turn and
+// stream them with whole-row 16-byte loads (the next step's loads in flight while this one
+// computes; K staged through LDS into MFMA operand order), compute S^T = K Q^T for the
+// packed query heads with v_mfma_f32_16x16x32_bf16 (query heads as the 16 MFMA columns), do
+// the online softmax on the VALU, and accumulate P V on the VALU with each lane owning D/16
+// head dims of one key in four. The four waves merge in LDS and write one fp32 partial per
+// (query head, chunk); the combine kernel merges the partials of each (sequence, query head).
+// The grid runs kv heads fastest, so the workgroups that share the cache rows of one key
+// range (the kv heads are interleaved within a row) are in flight together.
 // Decode is bound by HBM: every cached K/V byte is read exactly once.
 #include "fa_device.h"
 #include "fa_internal.h"
@@ -35,15 +38,20 @@ __device__ __forceinline__ float xor_sum(float x) {
 
 // D: head dim (64 or 128). GM: query heads per kv head the registers are sized for.
 template <int D, int GM>
-__global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecArgs a) {
+__global__ __launch_bounds__(kThreads, GM <= 4 ? 2 : 1) void decode_partial_kernel(DecArgs a) {
   constexpr int KS = D / 32;  // 32-dim MFMA steps
   constexpr int VE = D / 16;  // head dims per lane in the P V product
+  constexpr int CH = D / 8;     // 16-byte chunks per K/V row
+  constexpr int KPI = 64 / CH;  // keys per row-wise load instruction
+  __shared__ __attribute__((aligned(16))) char k_lds[4][kStep * D * 2];  // per-wave K staging
   __shared__ float p_lds[4][kStep][GM];
   __shared__ float alpha_lds[4][GM];
   __shared__ float m_lds[4][GM], l_lds[4][GM];
-  __shared__ float o_lds[4][GM][D];
+  // the cross-wave merge reuses the K staging area once every wave has left the key loop
+  static_assert(4 * GM * D * 4 <= sizeof(k_lds), "merge buffer");
+  float (*o_lds)[GM][D] = reinterpret_cast<float (*)[GM][D]>(&k_lds[0][0]);
 
-  const int chunk_id = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  const int hk = blockIdx.x, chunk_id = blockIdx.y, b = blockIdx.z;
   const int n = min(max(a.seqlens[b], 1), a.Nk_max);  // lengths outside [1, Nk_max] are clamped
   const int k_begin = chunk_id * a.chunk;
   if (k_begin >= n) return;  // past this sequence's length: nothing to read
@@ -73,42 +81,77 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecArgs a) {
     for (int e = 0; e < VE; ++e) acc[g][e] = 0.f;
   float m = kNegInf, l = 0.f;
 
-  const int per_wave = a.chunk / 4;
-  const int w_begin = k_begin + wave * per_wave;
-  const int w_end = min(k_end, w_begin + per_wave);
-  for (int base = w_begin; base < w_end; base += kStep) {
-    // ---- loads for 64 keys: K as MFMA A operand rows, V rows split over 16 lanes ----
-    u32x4 kr[4][KS];
-    const u32x4 zero = {0u, 0u, 0u, 0u};
+  // The four waves take the chunk's 64-key steps in turn (wave w: steps w, w + 4, ...), so at
+  // any moment a workgroup reads one contiguous run of cache rows.
+  const int w_begin = k_begin + wave * kStep;
+  const int w_end = k_end;
+  constexpr int kStride = 4 * kStep;
+
+  // K is read row-wise (CH lanes cover one key's row, KPI keys per instruction), which keeps
+  // every request a whole row segment, and staged through this wave's LDS area, from where
+  // the MFMA A-operand fragments (key kb*16 + l16, dims [32ks + 8g4, +8)) are read. Row
+  // chunks are XOR-swizzled by key so both the row-wise stores and the fragment reads are
+  // free of bank conflicts. V rows stay in registers split over 16 lanes (lane l16 owns dims
+  // [VE*l16, +VE) of keys 4s + g4). Loads go through a buffer resource that ends with the
+  // chunk's last key, so keys at or past w_end read as zeros without a memory access.
+  u32x4 kr[CH];
+  uint32_t vr[16][VE / 2];
+  // per-lane part of the offsets in a VGPR, the per-instruction row step in an SGPR
+  const int koff = (int)(((lane / CH) * a.k_row + (lane % CH) * 8) * 2);
+  const int voff = (int)((g4 * a.k_row + l16 * VE) * 2);
+  const int row_b = (int)(a.k_row * 2);
+  char* kl = k_lds[wave];
+  auto kswz = [](int key) { return D == 128 ? (key & 15) : ((key >> 1) & 7); };
+  auto load_k = [&](int base) {
+    const rsrc_t r = make_rsrc(kp + (long)base * a.k_row, ((long)(w_end - 1 - base) * a.k_row + D) * 2);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int key = base + kb * 16 + l16;
+    for (int i = 0; i < CH; ++i) kr[i] = __builtin_amdgcn_raw_buffer_load_b128(r, koff, i * KPI * row_b, 0);
+  };
+  auto stage_k = [&]() {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kr[kb][ks] = key < w_end ? *(const u32x4*)(kp + (long)key * a.k_row + ks * 32 + g4 * 8) : zero;
+    for (int i = 0; i < CH; ++i) {
+      const int key = i * KPI + lane / CH;
+      *(u32x4*)(kl + key * (D * 2) + (((lane % CH) ^ kswz(key)) << 4)) = kr[i];
     }
-    uint32_t vr[16][VE / 2];
+  };
+  auto load_v = [&](int base) {
+    const rsrc_t r = make_rsrc(vp + (long)base * a.k_row, ((long)(w_end - 1 - base) * a.k_row + D) * 2);
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
-      const int key = base + 4 * s + g4;
-      const uint16_t* src = vp + (long)key * a.k_row + l16 * VE;
       if (VE == 8) {
-        u32x4 t = key < w_end ? *(const u32x4*)src : zero;
+        const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 4 * s * row_b, 0);
 #pragma unroll
         for (int e = 0; e < VE / 2; ++e) vr[s][e] = t[e];
       } else {
-        u32x2 t = key < w_end ? *(const u32x2*)src : u32x2{0u, 0u};
+        const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 4 * s * row_b, 0);
 #pragma unroll
         for (int e = 0; e < VE / 2; ++e) vr[s][e] = t[e];
       }
     }
+  };
+
+  // Software pipeline over 64-key steps: the next step's K is requested as soon as this
+  // step's scores have consumed K, the next V as soon as the P V product has consumed V, so
+  // each load has a whole step of arithmetic to arrive in.
+  load_k(w_begin);
+  load_v(w_begin);
+  for (int base = w_begin; base < w_end; base += kStride) {
+    stage_k();
+    load_k(base + kStride);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // ---- scores: st[kb][r] is query head l16 against key base + 16kb + 4g4 + r ----
     f32x4 st[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       st[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int key = kb * 16 + l16;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) st[kb] = mfma_16x16x32(as_bf16x8(kr[kb][ks]), qf[ks], st[kb]);
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 f = *(const u32x4*)(kl + key * (D * 2) + (((4 * ks + g4) ^ kswz(key)) << 4));
+        st[kb] = mfma_16x16x32(as_bf16x8(f), qf[ks], st[kb]);
+      }
     }
     float mx = kNegInf;
 #pragma unroll
@@ -137,7 +180,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecArgs a) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // ---- rescale and accumulate P V: lane owns dims [VE*l16, +VE) of keys 4s + g4 ----
+    // ---- rescale and accumulate P V ----
 #pragma unroll
     for (int g = 0; g < GM; ++g) {
       const float al = alpha_lds[wave][g];
@@ -159,6 +202,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecArgs a) {
         }
       }
     }
+    load_v(base + kStride);
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -170,6 +214,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecArgs a) {
   for (int g = 0; g < GM; ++g)
 #pragma unroll
     for (int e = 0; e < VE; ++e) acc[g][e] = xor_sum(acc[g][e]);
+  __syncthreads();  // every wave is done with its K staging area, which now holds o_lds
   if (g4 == 0) {
     if (l16 < GM) {
       m_lds[wave][l16] = m;
@@ -225,7 +270,7 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecArgs a) {
 
 template <int D>
 hipError_t launch_d(const DecArgs& a, hipStream_t s) {
-  const dim3 grid((a.Nk_max + a.chunk - 1) / a.chunk, a.Hkv, a.B), block(kThreads);
+  const dim3 grid(a.Hkv, (a.Nk_max + a.chunk - 1) / a.chunk, a.B), block(kThreads);
   if (a.G <= 4) hipLaunchKernelGGL((decode_partial_kernel<D, 4>), grid, block, 0, s, a);
   else if (a.G <= 8) hipLaunchKernelGGL((decode_partial_kernel<D, 8>), grid, block, 0, s, a);
   else hipLaunchKernelGGL((decode_partial_kernel<D, 16>), grid, block, 0, s, a);

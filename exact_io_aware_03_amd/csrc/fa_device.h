@@ -65,6 +65,16 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer resource covering `bytes` from `base` (out-of-range loads return 0 without a
+// memory access, out-of-range stores are dropped). Word 3 selects 32-bit untyped access.
+// The range check applies to the 32-bit per-lane offset, so callers keep offsets below 2 GiB.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, long bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes >= 0x7fffffffL ? 0x7fffffff : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Hardware dispatches consecutive workgroup ids round-robin over the 8 XCDs. Give every XCD

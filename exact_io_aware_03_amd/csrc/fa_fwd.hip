@@ -45,7 +45,6 @@ constexpr float kTau = 8.f;              // rescale threshold, base-2 units (a f
 static_assert(BR == 32 * QH * kWaves, "rows per workgroup");
 constexpr int kF32Threads = 256;
 
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef __attribute__((address_space(3))) void lds_t;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -77,13 +76,6 @@ __device__ __forceinline__ int v_swz(int row) {
 template <int D>
 __device__ __forceinline__ int k_swz(int row) {
   return D == 128 ? (row & 15) : ((row >> 1) & 7);
-}
-
-// Raw buffer resource covering `bytes` from `base` (out-of-range loads return 0, out-of-range
-// stores are dropped). Word 3 selects 32-bit untyped access.
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, long bytes) {
-  const int n = bytes <= 0 ? 0 : (bytes >= 0x7fffffffL ? 0x7fffffff : (int)bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
 }
 
 // Per-lane global byte offsets of the direct-to-LDS loads of one tile: the instruction p of
@@ -320,9 +312,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5, l32 = lane & 31;
-  const int task = xcd_contiguous_task(blockIdx.x, a.n_tasks);
-  const int bh = task / a.n_qblk;
-  const int qb = CAUSAL ? a.n_qblk - 1 - task % a.n_qblk : task % a.n_qblk;  // longest first
+  // Non-causal: every task costs the same; each XCD takes a contiguous run of tasks so the
+  // query blocks of one head share that XCD's L2. Causal: dispatch order is longest first
+  // across all heads (every query block of the last row band, then the next band, ...).
+  int bh, qb;
+  if (CAUSAL) {
+    const int n_bh = a.n_tasks / a.n_qblk;
+    qb = a.n_qblk - 1 - (int)blockIdx.x / n_bh;
+    bh = (int)blockIdx.x % n_bh;
+  } else {
+    const int task = xcd_contiguous_task(blockIdx.x, a.n_tasks);
+    bh = task / a.n_qblk;
+    qb = task % a.n_qblk;
+  }
   const int b = bh / a.Hq, hq = bh % a.Hq, hk = hq / a.G;
 
   const uint16_t* qp = (const uint16_t*)a.q + (long)b * a.Nq * a.q_row + hq * D;
