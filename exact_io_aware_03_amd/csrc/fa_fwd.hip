@@ -122,12 +122,14 @@ __device__ __forceinline__ void dma_tile(char* buf, const uint16_t* kp, const ui
   }
 }
 
-// vmcnt-only wait (expcnt and lgkmcnt left unconstrained), then the workgroup barrier. Used
-// instead of __syncthreads so the direct-to-LDS loads of later tiles stay in flight.
+// Wait until at most N vector-memory loads are outstanding and this wave's LDS reads have
+// returned, then the workgroup barrier. Used instead of __syncthreads so the direct-to-LDS
+// loads of later tiles stay in flight; draining LDS reads first means no wave can pass the
+// barrier and refill a buffer that another wave is still reading.
 template <int N>
 __device__ __forceinline__ void wait_vm_barrier() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
   __builtin_amdgcn_s_barrier();
 }
 
@@ -226,35 +228,22 @@ __device__ __forceinline__ void tile_step(char* smem, int j, const uint16_t* kp,
   dma_tile<D>(smem + ((j + 3) % NBUF) * T::BUF, kp, vp, k_row, (j + 3) * BC, nk_load, dm);
   if (kv0 + BC > nk || (CAUSAL && kv0 + BC - 1 > q0)) mask_tile<CAUSAL>(s, kv0, nk, q0, l32, h);
 
-  // ---- phase A: scores of tile j+1 (MFMA) interleaved with the softmax of tile j (VALU) ----
-  f32x16 sn[QH][2];
-  if (NEXT) scores<D>(smem + ((j + 1) % NBUF) * T::BUF, krow0, h, qf, sn);
   // Conditional rescaling (Lecture 21 notes §5.3): the reference m only moves when the tile's
   // max exceeds it by more than kTau (base 2), so most tiles skip the O rescale; exponents stay
-  // <= kTau and the reference cancels in O = acc / l and in L = m + log2 l.
-  float alpha[QH];
+  // <= kTau and the reference cancels in O = acc / l and in L = m + log2 l. The rare rescale
+  // runs first, so the exponentials, the next tile's score MFMAs and the P V MFMAs below form
+  // one branch-free region that the scheduler can interleave.
+  float alpha[QH], m_use[QH];
   bool moved = false;
 #pragma unroll
   for (int qh = 0; qh < QH; ++qh) {
     const float mx = halves_max(max32(s[qh][0], s[qh][1])) * c;
     const bool up = mx > m[qh] + kTau;
     const float m_new = up ? mx : m[qh];
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    alpha[qh] = up ? fast_exp2(m[qh] - m_use) : 1.f;
+    m_use[qh] = m_new == kNegInf ? 0.f : m_new;
+    alpha[qh] = up ? fast_exp2(m[qh] - m_use[qh]) : 1.f;
     moved |= up;
     m[qh] = m_new;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[qh][kb][i] = fast_exp2(fmaf(s[qh][kb][i], c, -m_use));
-  }
-  if (NEXT) {
-#pragma unroll
-    for (int g = 0; g < 2 * (D / 16); ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one K fragment read
-      __builtin_amdgcn_sched_group_barrier(0x008, QH, 0);  // its MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // a slice of the softmax
-    }
   }
   if (__ballot(moved)) {
 #pragma unroll
@@ -265,6 +254,15 @@ __device__ __forceinline__ void tile_step(char* smem, int j, const uint16_t* kp,
         for (int i = 0; i < 16; ++i) o[qh][db][i] *= alpha[qh];
   }
 
+  // ---- phase A: scores of tile j+1 (MFMA) interleaved with the softmax of tile j (VALU) ----
+  f32x16 sn[QH][2];
+  if (NEXT) scores<D>(smem + ((j + 1) % NBUF) * T::BUF, krow0, h, qf, sn);
+#pragma unroll
+  for (int qh = 0; qh < QH; ++qh)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[qh][kb][i] = fast_exp2(fmaf(s[qh][kb][i], c, -m_use[qh]));
   // ---- phase B: O^T += V^T P^T (MFMA) interleaved with packing and the row sums (VALU) ----
 #pragma unroll
   for (int ks = 0; ks < BC / 16; ++ks) {
@@ -289,12 +287,6 @@ __device__ __forceinline__ void tile_step(char* smem, int j, const uint16_t* kp,
   }
 #pragma unroll
   for (int qh = 0; qh < QH; ++qh) l[qh] = l[qh] * alpha[qh] + sum32(s[qh][0], s[qh][1]);
-#pragma unroll
-  for (int g = 0; g < (BC / 16) * (D / 32); ++g) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two transposed V reads
-    __builtin_amdgcn_sched_group_barrier(0x008, QH, 0);  // their MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // packing / row sums
-  }
 
   wait_vm_barrier<T::VMCNT>();  // tile j+2 landed; tile j+3 may still be in flight
   if (NEXT) {
