@@ -96,6 +96,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   if (st != FA_OK) return st;
   if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
   if (causal && Nq != Nk) return FA_ERR_UNSUPPORTED;
+  // buffer-resource offsets are 32-bit: one batch of Q/dO or K/V must stay below 2 GiB
+  if ((long)Nq * Hq * d * 2 >= (1L << 31) || (long)Nk * Hkv * d * 2 >= (1L << 31)) return FA_ERR_UNSUPPORTED;
   const size_t need = fa_bwd_workspace_size(B, Hq, Nq, d);
   if (!workspace || ws_bytes < need || !aligned16(workspace)) return FA_ERR_WORKSPACE;
   fa::BwdArgs a{};

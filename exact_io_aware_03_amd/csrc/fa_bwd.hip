@@ -7,13 +7,21 @@
 // loop runs over K/V blocks so dK and dV stay on chip and only dQ is accumulated across
 // workgroups with atomic adds (half the atomics of a query-outer order).
 //
-// gfx950 mapping: a workgroup owns 128 keys (32 per wave) of one (batch, kv head) and walks
-// the 64-row query blocks that can see them (causal: only blocks at or below the diagonal,
-// longest task first), for every query head of the GQA group. Scores come out of the MFMA
-// with one key per lane, so P^T and dS^T feed the dV and dK products straight from the
-// accumulators (query rows relabelled as in the forward); Q and dO sit in LDS both row-major
-// (score operands) and transposed (dV/dK operands); dS goes through LDS once for the dQ
-// product, whose result rows map to coalesced fp32 global atomics.
+// gfx950 mapping: a workgroup owns 128 keys (32 per wave, one wave per SIMD) of one
+// (batch, kv head) and walks the 64-row query blocks that can see them (causal: only blocks at
+// or below the diagonal, longest task first), for every query head of the GQA group, as one
+// flat sequence of steps. Per step:
+//  * Q, dO (row-major) and L, D of the next step stream into the other half of a double
+//    buffer with direct-to-LDS loads while this step computes;
+//  * S = Q K^T and dP = dO V^T come out of the MFMA with one key per lane (K and V rows sit in
+//    registers for the whole task), so P^T and dS^T feed the dV and dK products straight from
+//    the accumulators (query rows relabelled as in the forward); the B operands of those
+//    products (dO and Q with 8 consecutive rows per lane) are read transposed from the same
+//    row-major tiles with ds_read_b64_tr_b16, one XOR swizzle serving both access patterns;
+//  * dS^T goes to LDS with 16-byte stores and comes back transposed as the A operand of
+//    dQ = dS K (K row-major in LDS for the whole task); each wave owns two 32x32 dQ tiles whose
+//    rows map to coalesced fp32 global atomics.
+// Two barriers per step: one after this step's tiles have landed, one after dS^T is complete.
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -21,46 +29,128 @@ namespace fa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
 constexpr int BK = kBwdKeys;  // 128 keys per workgroup
-constexpr int BQ = kBwdRows;  // 64 query rows per inner step
+constexpr int BQ = kBwdRows;  // 64 query rows per step
 
-__device__ __forceinline__ int t_swz(int d) { return (d ^ (d >> 3)) & 7; }
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Chunk swizzle of the row-major Q, dO and K tiles (16-byte chunks XOR-ed with a function of
+// the row). Row reads (16 lanes, 16 rows, one logical chunk) need a bijection of the row's low
+// 4 bits (d=128: 16 chunks per 256-byte row) or of bits 1-3 (d=64: two 128-byte rows per bank
+// line); transposed reads (16 lanes, 4 consecutive rows x 32 bytes) need the 4 rows to differ in
+// chunk bits 2-3. Swapping the two 2-bit halves of the row's low nibble does both at d=128.
+template <int D>
+__device__ __forceinline__ int t_swz(int row) {
+  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((row >> 1) & 7);
+}
+// dS^T tile [key][query], 128-byte rows.
+__device__ __forceinline__ int ds_swz(int row) { return (row >> 1) & 7; }
 
 template <int D>
 struct BwdLds {
-  static constexpr int KCH = D / 8;
-  static constexpr int QN = BQ * D * 2;   // Q, row-major [q][d]
-  static constexpr int QT = D * BQ * 2;   // Q^T, [d][q]
-  static constexpr int KT = D * BK * 2;   // K^T, [d][key]
-  static constexpr int DS = BQ * BK * 2;  // dS, [q][key]
-  static constexpr int OFF_QN = 0;
-  static constexpr int OFF_DON = OFF_QN + QN;
-  static constexpr int OFF_QT = OFF_DON + QN;
-  static constexpr int OFF_DOT = OFF_QT + QT;
-  static constexpr int OFF_KT = OFF_DOT + QT;
-  static constexpr int OFF_DS = OFF_KT + KT;
-  static constexpr int OFF_L = OFF_DS + DS;
-  static constexpr int OFF_D = OFF_L + BQ * 4;
-  static constexpr int BYTES = OFF_D + BQ * 4;
+  static constexpr int ROW = D * 2;
+  static constexpr int KT = BK * ROW;    // K, row-major [key][d]
+  static constexpr int QT = BQ * ROW;    // one Q or dO tile, row-major [q][d]
+  static constexpr int DST = BK * BQ * 2;  // dS^T, [key][q]
+  static constexpr int OFF_K = 0;
+  static constexpr int OFF_Q = OFF_K + KT;         // Q[2]
+  static constexpr int OFF_DO = OFF_Q + 2 * QT;    // dO[2]
+  static constexpr int OFF_DS = OFF_DO + 2 * QT;
+  static constexpr int OFF_L = OFF_DS + DST;       // L[2][BQ] fp32 (natural log)
+  static constexpr int OFF_D = OFF_L + 2 * BQ * 4;  // D[2][BQ] fp32
+  static constexpr int BYTES = OFF_D + 2 * BQ * 4;
+  static constexpr int RR = 1024 / ROW;            // rows per 1 KiB direct-to-LDS load
+  static constexpr int QDMA = QT / 1024 / kWaves;  // loads per wave per Q or dO tile
+  static constexpr int KDMA = KT / 1024 / kWaves;  // loads per wave for the K tile
+  static constexpr int STEP_DMA = 2 * QDMA + 2;    // Q, dO, L, D
 };
 
-// Transpose a 4-row x 8-dim block held as four 16-byte words into eight 8-byte column
-// pieces, writing them to a [dim][row] LDS array with `pitch` bytes per dim row.
-__device__ __forceinline__ void write_transposed(char* base, int pitch, int rg, int dc, const u32x4 (&w)[4]) {
+// Raw buffer resource as four scalar words (base, stride 0, size, 32-bit untyped format).
+__device__ __forceinline__ u32x4 dma_rsrc(const void* base, long bytes) {
+  const unsigned long long p = (unsigned long long)base;
+  u32x4 r;
+  r[0] = (uint32_t)p;
+  r[1] = (uint32_t)(p >> 32) & 0xffffu;
+  r[2] = bytes <= 0 ? 0u : (bytes >= 0x7fffffffL ? 0x7fffffffu : (uint32_t)bytes);
+  r[3] = 0x00020000u;
+  return r;
+}
+
+// Wave-wide direct-to-LDS loads: lane i's 16 (or 4) bytes land at dst + 16 i (4 i). Inline asm
+// so that the compiler does not wait for these loads before unrelated LDS reads; completion is
+// ordered explicitly with s_waitcnt vmcnt before the barrier that publishes a tile.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 is written by the asm itself
+__device__ __forceinline__ void lds_dma16(const u32x4& r, char* dst, int voff) {
+  const uint32_t m0 =
+      __builtin_amdgcn_readfirstlane((uint32_t)(size_t)((__attribute__((address_space(3))) char*)dst));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(const u32x4& r, char* dst, int voff) {
+  const uint32_t m0 =
+      __builtin_amdgcn_readfirstlane((uint32_t)(size_t)((__attribute__((address_space(3))) char*)dst));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Scheduling fence: no instruction moves across it.
+__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Wait until at most N vector-memory operations of this wave are pending and its LDS accesses
+// are done, then the workgroup barrier. The empty asm statements keep the compiler from moving
+// memory accesses across.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+// The same for LDS only: vector-memory operations (prefetches, atomics) stay in flight.
+__device__ __forceinline__ void lds_barrier() { wait_vm_barrier<63>(); }
+
+// This wave's share of the direct-to-LDS loads of `rows` rows of a row-major [*, D] bf16 tensor
+// into a swizzled LDS tile: load p of wave w fills 1 KiB (region kWaves*p + w), lane i landing
+// on row RR*region + i/KCH, physical chunk i%KCH, and fetching the logical chunk the swizzle
+// puts there. Rows at or past `valid_rows` read as zero.
+template <int D, int NLOAD>
+__device__ __forceinline__ void dma_rows(char* dst, const uint16_t* src, long row_stride, int valid_rows) {
+  using L = BwdLds<D>;
+  constexpr int KCH = D / 8;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const u32x4 r = dma_rsrc(src, ((long)(valid_rows - 1) * row_stride + D) * 2);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int d = dc * 8 + i;
-    const uint32_t w0 = w[0][i >> 1], w1 = w[1][i >> 1], w2 = w[2][i >> 1], w3 = w[3][i >> 1];
-    u32x2 out;
-    if (i & 1) {
-      out[0] = (w0 >> 16) | (w1 & 0xffff0000u);
-      out[1] = (w2 >> 16) | (w3 & 0xffff0000u);
-    } else {
-      out[0] = (w0 & 0xffffu) | (w1 << 16);
-      out[1] = (w2 & 0xffffu) | (w3 << 16);
-    }
-    *(u32x2*)(base + d * pitch + (((rg >> 1) ^ t_swz(d)) << 4) + ((rg & 1) << 3)) = out;
+  for (int p = 0; p < NLOAD; ++p) {
+    const int region = kWaves * p + w;
+    const int row = L::RR * region + lane / KCH, pc = lane % KCH;
+    const int voff = (int)((row * row_stride + ((pc ^ t_swz<D>(row)) * 8)) * 2);
+    lds_dma16(r, dst + region * 1024, voff);
   }
+}
+
+// A operand of a transposed product read from a row-major LDS tile with two
+// ds_read_b64_tr_b16: lane l receives column c0 + l%32 (c0 = 32*cb) and the 8 consecutive rows
+// 16ks + 8(l/32) .. +7. In each 16-lane group, source lane s points at row r0 + s/4,
+// columns 16((l/16)%2) + 4(s%4) .. +3 of the block.
+template <int ROWB, typename Swz>
+__device__ __forceinline__ bf16x8 tr_frag(const char* base, int ks, int cb, int lane, Swz swz) {
+  const int s = lane & 15, g = lane >> 4;
+  i16x4 r[2];
+#pragma unroll
+  for (int rd = 0; rd < 2; ++rd) {
+    const int row = 16 * ks + 8 * (g >> 1) + 4 * rd + (s >> 2);
+    const int col_b = (32 * cb + 16 * (g & 1) + 4 * (s & 3)) * 2;  // byte column
+    const int off = row * ROWB + (((col_b >> 4) ^ swz(row)) << 4) + (col_b & 15);
+    r[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off));
+  }
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 c = __builtin_shufflevector(r[0], r[1], 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
 }
 
 // D = rowsum(dO * O) per (batch, head, row) and a zeroed fp32 dQ accumulator. One wave per row.
@@ -94,188 +184,190 @@ __global__ __launch_bounds__(kThreads) void bwd_post_kernel(BwdArgs a, long n) {
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   using L = BwdLds<D>;
+  constexpr int KS = D / 16, DB = D / 32;
+  constexpr int TILES = 2 * DB / kWaves;  // 32x32 dQ tiles per wave
+  constexpr int NA = TILES * 16;          // dQ atomic instructions per wave and full step
+  static_assert(NA + L::STEP_DMA < 64, "vmcnt range");
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
-  char* qn = smem + L::OFF_QN;
-  char* don = smem + L::OFF_DON;
-  char* qt = smem + L::OFF_QT;
-  char* dot_ = smem + L::OFF_DOT;
-  char* kt = smem + L::OFF_KT;
+  char* kl = smem + L::OFF_K;
   char* dsl = smem + L::OFF_DS;
-  float* l2s = (float*)(smem + L::OFF_L);
-  float* dls = (float*)(smem + L::OFF_D);
 
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int h = lane >> 5, l32 = lane & 31;
-  const int task = xcd_contiguous_task(blockIdx.x, a.n_tasks);
-  const int bhk = task / a.n_kvblk, j = task % a.n_kvblk;  // j ascending: longest first
+  // causal: kv block 0 sees every query block; dispatch order is longest first over all
+  // (batch, kv head) pairs. Non-causal: XCD-contiguous ranges of one (batch, kv head).
+  int bhk, j;
+  if (a.causal) {
+    const int n_bhk = a.n_tasks / a.n_kvblk;
+    j = (int)blockIdx.x / n_bhk;
+    bhk = (int)blockIdx.x % n_bhk;
+  } else {
+    const int task = xcd_contiguous_task(blockIdx.x, a.n_tasks);
+    bhk = task / a.n_kvblk;
+    j = task % a.n_kvblk;
+  }
   const int b = bhk / a.Hkv, hk = bhk % a.Hkv;
   const int kv0 = j * BK;
   const int kw0 = kv0 + wave * 32;  // this wave's keys
   const int key = kw0 + l32;        // this lane's key
   const uint16_t* kp = (const uint16_t*)a.k + (long)b * a.Nk * a.k_row + hk * D;
   const uint16_t* vp = (const uint16_t*)a.v + (long)b * a.Nk * a.k_row + hk * D;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
 
-  // K^T, V^T as B operands of S = Q K^T and dP = dO V^T: lane holds key, dims [16ks+8h, +8)
-  bf16x8 kf[D / 16], vf[D / 16];
+  // K, V rows as B operands of S = Q K^T and dP = dO V^T: lane holds key, dims [16ks+8h, +8)
+  bf16x8 kf[KS], vf[KS];
+  {
+    const long valid = ((long)(a.Nk - 1) * a.k_row + D) * 2;
+    const rsrc_t rk = make_rsrc(kp, valid), rv = make_rsrc(vp, valid);
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    const bool ok = key < a.Nk;
-    kf[ks] = as_bf16x8(ok ? *(const u32x4*)(kp + (long)key * a.k_row + ks * 16 + h * 8) : zero);
-    vf[ks] = as_bf16x8(ok ? *(const u32x4*)(vp + (long)key * a.k_row + ks * 16 + h * 8) : zero);
-  }
-  // K^T of the workgroup's 128 keys into LDS for the dQ product.
-  for (int blk = t; blk < (BK / 4) * L::KCH; blk += kThreads) {
-    const int rg = blk / L::KCH, dc = blk % L::KCH;
-    u32x4 w[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int kk = kv0 + 4 * rg + r;
-      w[r] = kk < a.Nk ? *(const u32x4*)(kp + (long)kk * a.k_row + dc * 8) : zero;
+    for (int ks = 0; ks < KS; ++ks) {
+      const int off = (int)(((long)key * a.k_row + ks * 16 + h * 8) * 2);
+      kf[ks] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+      vf[ks] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
     }
-    write_transposed(kt, BK * 2, rg, dc, w);
   }
+  // the compiler does not count the asm loads below: its own loads complete first
+  __builtin_amdgcn_s_waitcnt(0);
+  // K rows of the whole block, row-major, for the dQ product
+  dma_rows<D, L::KDMA>(kl, kp + (long)kv0 * a.k_row, a.k_row, a.Nk - kv0);
 
-  f32x16 dk[D / 32], dv[D / 32];
+  f32x16 dk[DB], dv[DB];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) dk[db][i] = dv[db][i] = 0.f;
 
   const int n_qblk = (a.Nq + BQ - 1) / BQ;
   const int qb_first = a.causal ? kv0 / BQ : 0;
-  const int arow = swap_bits23(l32);
+  const int per_head = n_qblk - qb_first;
+  const int n_steps = a.G * per_head;
 
-  for (int hq = hk * a.G; hq < (hk + 1) * a.G; ++hq) {
-    const uint16_t* qp = (const uint16_t*)a.q + (long)b * a.Nq * a.q_row + hq * D;
-    const uint16_t* gp = (const uint16_t*)a.dout + (long)b * a.Nq * a.q_row + hq * D;
-    const float* lp = a.lse + ((long)b * a.Hq + hq) * a.Nq;
-    const float* dp = a.dvec + ((long)b * a.Hq + hq) * a.Nq;
-    for (int qb = qb_first; qb < n_qblk; ++qb) {
-      const int q0 = qb * BQ;
-      // ---- stage Q and dO (row-major and transposed), L (base 2) and D ----
-      for (int blk = t; blk < (BQ / 4) * L::KCH; blk += kThreads) {
-        const int rg = blk / L::KCH, dc = blk % L::KCH;
-        u32x4 wq[4], wg[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int qq = q0 + 4 * rg + r;
-          const bool ok = qq < a.Nq;
-          wq[r] = ok ? *(const u32x4*)(qp + (long)qq * a.q_row + dc * 8) : zero;
-          wg[r] = ok ? *(const u32x4*)(gp + (long)qq * a.q_row + dc * 8) : zero;
-          const int row = 4 * rg + r;
-          const int off = row * (D * 2) + ((dc ^ swz_perm_rows(row)) << 4);
-          *(u32x4*)(qn + off) = wq[r];
-          *(u32x4*)(don + off) = wg[r];
-        }
-        write_transposed(qt, BQ * 2, rg, dc, wq);
-        write_transposed(dot_, BQ * 2, rg, dc, wg);
-      }
-      if (t < BQ) {
-        const int qq = q0 + t;
-        l2s[t] = qq < a.Nq ? lp[qq] * kLog2e : __builtin_inff();  // rows past Nq: P = 0
-        dls[t] = qq < a.Nq ? dp[qq] : 0.f;
-      }
-      __syncthreads();
+  // Issue the loads of step st (query head hk*G + st/per_head, block qb_first + st%per_head)
+  // into buffer st&1: Q and dO tiles, then L and D (one 4-byte load per lane each).
+  auto issue_step = [&](int st) {
+    const int hq = hk * a.G + st / per_head, q0 = (qb_first + st % per_head) * BQ;
+    const int buf = st & 1;
+    const long qoff = ((long)b * a.Nq + q0) * a.q_row + hq * D;
+    dma_rows<D, L::QDMA>(smem + L::OFF_Q + buf * L::QT, (const uint16_t*)a.q + qoff, a.q_row, a.Nq - q0);
+    dma_rows<D, L::QDMA>(smem + L::OFF_DO + buf * L::QT, (const uint16_t*)a.dout + qoff, a.q_row, a.Nq - q0);
+    const long loff = ((long)b * a.Hq + hq) * a.Nq + q0;
+    const long lbytes = (long)min(BQ, a.Nq - q0) * 4;
+    lds_dma4(dma_rsrc(a.lse + loff, lbytes), smem + L::OFF_L + buf * BQ * 4, lane * 4);
+    lds_dma4(dma_rsrc(a.dvec + loff, lbytes), smem + L::OFF_D + buf * BQ * 4, lane * 4);
+  };
 
-      const bool wave_live = !a.causal || kw0 <= q0 + BQ - 1;
-      if (wave_live) {
-        // ---- S = Q K^T and dP = dO V^T for 64 rows x this wave's 32 keys ----
-        f32x16 s[2], g[2];
-#pragma unroll
-        for (int qh = 0; qh < 2; ++qh) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) s[qh][i] = g[qh][i] = 0.f;
-          const int row = 32 * qh + arow;
-          const int sw = swz_perm_rows(row);
-#pragma unroll
-          for (int ks = 0; ks < D / 16; ++ks) {
-            const int off = row * (D * 2) + (((2 * ks + h) ^ sw) << 4);
-            s[qh] = mfma_32x32x16(*(const bf16x8*)(qn + off), kf[ks], s[qh]);
-            g[qh] = mfma_32x32x16(*(const bf16x8*)(don + off), vf[ks], g[qh]);
-          }
-        }
-        // register i of half qh holds query row 32qh + (i&7) + 8h + 16(i>>3) and key `key`
-#pragma unroll
-        for (int qh = 0; qh < 2; ++qh) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int r = 32 * qh + (i & 7) + 8 * h + 16 * (i >> 3);
-            float p = fast_exp2(fmaf(s[qh][i], a.c, -l2s[r]));
-            if (key >= a.Nk || (a.causal && key > q0 + r)) p = 0.f;
-            s[qh][i] = p;                         // P
-            g[qh][i] = p * (g[qh][i] - dls[r]);  // dS
-          }
-        }
-        // ---- dV += P^T dO, dK += dS^T Q over the 64 rows (16 per step) ----
-#pragma unroll
-        for (int kq = 0; kq < BQ / 16; ++kq) {
-          const int e = (kq & 1) * 8;
-          const f32x16& ps = s[kq >> 1];
-          const f32x16& gs = g[kq >> 1];
-          u32x4 pw, gw;
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            pw[x] = pack_bf16x2(ps[e + 2 * x], ps[e + 2 * x + 1]);
-            gw[x] = pack_bf16x2(gs[e + 2 * x], gs[e + 2 * x + 1]);
-          }
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            const int d = 32 * db + l32;
-            const int off = d * (BQ * 2) + (((2 * kq + h) ^ t_swz(d)) << 4);
-            dv[db] = mfma_32x32x16(as_bf16x8(pw), *(const bf16x8*)(dot_ + off), dv[db]);
-            dk[db] = mfma_32x32x16(as_bf16x8(gw), *(const bf16x8*)(qt + off), dk[db]);
-          }
-        }
-        // ---- dS (bf16) to LDS, row-major [q][key] for the dQ product ----
-#pragma unroll
-        for (int qh = 0; qh < 2; ++qh)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int r = 32 * qh + (i & 7) + 8 * h + 16 * (i >> 3);
-            const int kc = wave * 32 + l32;
-            *(__bf16*)(dsl + r * (BK * 2) + ((((kc >> 3) ^ (r & 7))) << 4) + ((kc & 7) << 1)) =
-                (__bf16)g[qh][i];
-          }
-      } else {
-        // all 64 rows are above this wave's keys: its dS columns are zero
-        const int kc = wave * 32 + l32;
-        for (int r = 32 * h; r < 32 * h + 32; ++r)
-          *(__bf16*)(dsl + r * (BK * 2) + ((((kc >> 3) ^ (r & 7))) << 4) + ((kc & 7) << 1)) = (__bf16)0.f;
-      }
-      __syncthreads();
-
-      // ---- dQ[64 x D] += dS[64 x 128] K[128 x D]: each wave computes 32-row x 32-dim tiles ----
-      {
-        constexpr int NT = 2 * (D / 32);  // output tiles
-        for (int tile = wave; tile < NT; tile += 4) {
-          const int qt_ = tile / (D / 32), db = tile % (D / 32);
-          f32x16 acc;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-          const int r = 32 * qt_ + l32;
-          const int d = 32 * db + l32;
-#pragma unroll
-          for (int ks = 0; ks < BK / 16; ++ks) {
-            const bf16x8 af = *(const bf16x8*)(dsl + r * (BK * 2) + (((2 * ks + h) ^ (r & 7)) << 4));
-            const bf16x8 bfr = *(const bf16x8*)(kt + d * (BK * 2) + (((2 * ks + h) ^ t_swz(d)) << 4));
-            acc = mfma_32x32x16(af, bfr, acc);
-          }
-          // register i holds row 32qt + 8(i/4) + 4h + i%4, dim d
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int qq = q0 + 32 * qt_ + 8 * (i >> 2) + 4 * h + (i & 3);
-            if (qq < a.Nq) unsafeAtomicAdd(a.dq_acc + (((long)b * a.Nq + qq) * a.Hq + hq) * D + d, acc[i]);
-          }
-        }
-      }
-      __syncthreads();
+  issue_step(0);
+  bool prev_full = true;  // the previous step issued all NA dQ atomics
+  for (int st = 0; st < n_steps; ++st) {
+    const int hq = hk * a.G + st / per_head, q0 = (qb_first + st % per_head) * BQ;
+    const bool has_next = st + 1 < n_steps;
+    if (has_next) issue_step(st + 1);
+    // This step's loads are complete once at most the loads issued after them are pending:
+    // the previous step's dQ atomics (when it issued all of them) and the next step's tiles.
+    if (has_next) {
+      if (st > 0 && prev_full) wait_vm_barrier<NA + L::STEP_DMA>();
+      else wait_vm_barrier<L::STEP_DMA>();
+    } else {
+      if (st > 0 && prev_full) wait_vm_barrier<NA>();
+      else wait_vm_barrier<0>();
     }
+    // LDS addresses are recomputed each step from a pinned copy of the lane index instead of
+    // being hoisted out of the loop: VALU time is cheap here, registers are not.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int lh = ln >> 5, ll = ln & 31;
+    const int buf = st & 1;
+    const char* ql = smem + L::OFF_Q + buf * L::QT;
+    const char* dol = smem + L::OFF_DO + buf * L::QT;
+    const float* lls = (const float*)(smem + L::OFF_L + buf * BQ * 4);
+    const float* dls = (const float*)(smem + L::OFF_D + buf * BQ * 4);
+
+    // (causal blocks entirely above this wave's keys run too: their P is masked to zero)
+    // ---- S = Q K^T and dP = dO V^T for 64 rows x this wave's 32 keys ----
+    f32x16 s[2], g[2];
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      zero16(s[qh]);
+      zero16(g[qh]);
+      const int row = 32 * qh + swap_bits23(ll);
+      const int sw = t_swz<D>(row);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int off = row * L::ROW + (((2 * ks + lh) ^ sw) << 4);
+        s[qh] = mfma_32x32x16(*(const bf16x8*)(ql + off), kf[ks], s[qh]);
+        g[qh] = mfma_32x32x16(*(const bf16x8*)(dol + off), vf[ks], g[qh]);
+      }
+      fence();  // bounds the operand reads in flight (register budget)
+    }
+    // register i of half qh holds query row 32qh + (i&7) + 8h + 16(i>>3) and key `key`
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = 32 * qh + (i & 7) + 8 * h + 16 * (i >> 3);
+        float p = fast_exp2(fmaf(s[qh][i], a.c, -lls[r] * kLog2e));
+        if (key >= a.Nk || (a.causal && key > q0 + r)) p = 0.f;
+        s[qh][i] = p;                         // P
+        g[qh][i] = p * (g[qh][i] - dls[r]);  // dS
+      }
+    }
+    // ---- dV += P^T dO, dK += dS^T Q over the 64 rows (16 per step); dS^T to LDS ----
+#pragma unroll
+    for (int kq = 0; kq < BQ / 16; ++kq) {
+      const int e = (kq & 1) * 8;
+      const f32x16& ps = s[kq >> 1];
+      const f32x16& gs = g[kq >> 1];
+      u32x4 pw, gw;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        pw[x] = pack_bf16x2(ps[e + 2 * x], ps[e + 2 * x + 1]);
+        gw[x] = pack_bf16x2(gs[e + 2 * x], gs[e + 2 * x + 1]);
+      }
+      const int kc = wave * 32 + ll;
+      *(u32x4*)(dsl + kc * (BQ * 2) + (((2 * kq + lh) ^ ds_swz(kc)) << 4)) = gw;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        dv[db] = mfma_32x32x16(as_bf16x8(pw), tr_frag<L::ROW>(dol, kq, db, ln, t_swz<D>), dv[db]);
+        dk[db] = mfma_32x32x16(as_bf16x8(gw), tr_frag<L::ROW>(ql, kq, db, ln, t_swz<D>), dk[db]);
+      }
+      fence();
+    }
+    lds_barrier();  // dS^T complete
+
+    // ---- dQ[64 x D] += dS[64 x 128] K[128 x D]; tile tt = (query half tt%2, dim block tt/2) ----
+    const bool full = q0 + BQ <= a.Nq;
+#pragma unroll
+    for (int u = 0; u < TILES; ++u) {
+      const int tt = wave + kWaves * u;
+      const int qh = tt & 1, db = tt >> 1;
+      f32x16 acc;
+      zero16(acc);
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        acc = mfma_32x32x16(tr_frag<BQ * 2>(dsl, ks, qh, ln, ds_swz), tr_frag<L::ROW>(kl, ks, db, ln, t_swz<D>),
+                            acc);
+        if (ks % 4 == 3) fence();
+      }
+      // register i holds query row 32qh + 8(i/4) + 4h + i%4, dim 32db + l32
+      float* dst = a.dq_acc + (((long)b * a.Nq + q0 + 32 * qh + 4 * h) * a.Hq + hq) * D + 32 * db + l32;
+      const long rs = (long)a.Hq * D;
+      if (full) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) unsafeAtomicAdd(dst + (8 * (i >> 2) + (i & 3)) * rs, acc[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (q0 + 32 * qh + 8 * (i >> 2) + 4 * h + (i & 3) < a.Nq)
+            unsafeAtomicAdd(dst + (8 * (i >> 2) + (i & 3)) * rs, acc[i]);
+      }
+    }
+    prev_full = full;
   }
+  __builtin_amdgcn_s_waitcnt(0);
 
   // ---- dK = scale * acc, dV = acc (bf16); register i holds key kw0 + 8(i/4) + 4h + i%4 ----
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int kk = kw0 + 8 * (i >> 2) + 4 * h + (i & 3);

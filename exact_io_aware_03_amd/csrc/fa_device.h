@@ -75,6 +75,11 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, long bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
 }
 
+__device__ __forceinline__ void zero16(f32x16& x) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = 0.f;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Hardware dispatches consecutive workgroup ids round-robin over the 8 XCDs. Give every XCD

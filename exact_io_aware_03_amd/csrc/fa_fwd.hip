@@ -133,11 +133,6 @@ __device__ __forceinline__ void wait_vm_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-__device__ __forceinline__ void zero16(f32x16& x) {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) x[i] = 0.f;
-}
-
 // Scores of this wave's rows against the 64 keys of one LDS tile: s[qh][kb] = K_kb Q_qh^T.
 template <int D>
 __device__ __forceinline__ void scores(const char* kt, int krow0, int h, const bf16x8 (&qf)[QH][D / 16],
