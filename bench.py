@@ -2,13 +2,16 @@
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
 
-A step is one pass of the training-shape forward (B=16, H=16, N=2048, d=128, bf16) without
-and with the causal mask. `value` is the step's algorithmic TFLOP/s (4*N_q*N_k*d per head
-without a mask; 4*d*N(N+1)/2 with it). The same run also times the long-context causal
-forward, the ragged GQA decode (HBM GB/s) and the causal backward, each with HIP events on
-the stream the library launches on, and times the fp64 CPU oracle on a bounded sample of the
-training-shape workload (`cpu_baseline`). Inputs are the seeded synthetic tensors of
-workloads.py, resident in device memory before any timed region. One JSON line on stdout.
+A step is one training pass of the hot path on the training-shape workload (B=16, H=16,
+N=2048, d=128, bf16): fa_fwd then fa_bwd (recomputing P from the saved L), without and with the
+causal mask. `value` is the step's algorithmic TFLOP/s: 4*N_q*N_k*d per head for a forward and
+10*N_q*N_k*d for a backward (five products, the recomputation of S included) over the visible
+pairs (N(N+1)/2 with the causal mask). The ragged GQA decode is an inference path of its own
+and is reported in `results` in HBM GB/s, as are the long-context causal forward and the
+causal backward of the backward workload. Every kernel time comes from HIP events on the stream
+the library launches on. The fp64 CPU oracle is timed on a bounded sample of the training-shape
+forward (`cpu_baseline`). Inputs are the seeded synthetic tensors of workloads.py, resident in
+device memory before any timed region. One JSON line on stdout.
 """
 
 from __future__ import annotations
@@ -133,18 +136,27 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # ---- the step: training-shape forward, without and with the causal mask ----
+    # ---- the step: training-shape forward + backward, without and with the causal mask ----
     w = workloads.WORKLOADS["fwd_bf16_b16h16n2048d128"]
-    log(f"[bench] generating {w.name}")
-    inp = workloads.make_workload_inputs(w)
-    q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+    log(f"[bench] generating {w.name} (+ dO from the same seeded stream)")
+    inp = workloads.make_attention_inputs(w.B, w.Nq, w.Nk, w.Hq, w.Hkv, w.d, w.seed, w.dtype, with_do=True)
+    q, k, v, do = dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["do"])
     del inp
-    o = torch.empty_like(q)
-    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda")
+    o = {m: torch.empty_like(q) for m in (False, True)}
+    lse = {m: torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda") for m in (False, True)}
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.Hq, w.Nq, w.d), dtype=torch.uint8, device="cuda")
+
+    def fwd(m):
+        fa.fa_fwd(q, k, v, o[m], lse[m], causal=m, scale=w.scale)
+
+    def bwd(m):
+        fa.fa_bwd(q, k, v, o[m], do, lse[m], dq, dk, dv, ws, causal=m, scale=w.scale)
 
     def step():
-        fa.fa_fwd(q, k, v, o, lse, causal=False, scale=w.scale)
-        fa.fa_fwd(q, k, v, o, lse, causal=True, scale=w.scale)
+        for m in (False, True):
+            fwd(m)
+            bwd(m)
 
     for _ in range(args.warmup):
         step()
@@ -154,27 +166,32 @@ def main():
         step()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    step_flops = fwd_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, False) + fwd_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, True)
+    ff = {m: fwd_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, m) for m in (False, True)}
+    bf = {m: bwd_flops(w.B, w.Hq, w.Nq, w.d, m) for m in (False, True)}
+    step_flops = sum(ff.values()) + sum(bf.values())
     value = step_flops * args.steps / dt / 1e12
     log(f"[bench] step: {dt / args.steps * 1e3:.3f} ms, {value:.1f} TFLOP/s")
 
-    # ---- the dominant kernel: the non-causal forward launch, HIP events on the launch stream ----
-    nc_ms = time_launches(lambda: fa.fa_fwd(q, k, v, o, lse, causal=False, scale=w.scale), args.reps * 2, 3)
-    c_ms = time_launches(lambda: fa.fa_fwd(q, k, v, o, lse, causal=True, scale=w.scale), args.reps * 2, 3)
-    nc_avg = float(np.mean(nc_ms))
-    f_nc = fwd_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, False)
-    achieved = f_nc / (nc_avg * 1e-3) / 1e12
-    results = {
-        "fwd_nc_b16h16n2048d128": {"ms": round(nc_avg, 4), "tflops": round(achieved, 2),
-                                    "frac_peak": round(achieved / PEAK_BF16_TFLOPS, 4)},
-        "fwd_causal_b16h16n2048d128": {
-            "ms": round(float(np.mean(c_ms)), 4),
-            "tflops": round(fwd_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, True) / (np.mean(c_ms) * 1e-3) / 1e12, 2),
-        },
-    }
-    results["fwd_causal_b16h16n2048d128"]["frac_peak"] = round(
-        results["fwd_causal_b16h16n2048d128"]["tflops"] / PEAK_BF16_TFLOPS, 4)
-    del q, k, v, o, lse
+    # ---- per-call times of the step's parts, HIP events on the launch stream ----
+    results = {}
+    part_ms = {}
+    for m in (False, True):
+        tag = "causal" if m else "nc"
+        f_ms = float(np.mean(time_launches(lambda: fwd(m), args.reps * 2, 3)))
+        b_ms = float(np.mean(time_launches(lambda: bwd(m), args.reps, 2)))
+        part_ms[("fwd", m)], part_ms[("bwd", m)] = f_ms, b_ms
+        for kind, ms, fl in (("fwd", f_ms, ff[m]), ("bwd", b_ms, bf[m])):
+            tf = fl / (ms * 1e-3) / 1e12
+            results[f"{kind}_{tag}_b16h16n2048d128"] = {"ms": round(ms, 4), "tflops": round(tf, 2),
+                                                        "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    # the dominant part of the step: the call with the largest share of the step's time
+    dom = max(part_ms, key=part_ms.get)
+    dom_ms = part_ms[dom]
+    dom_flops = (ff if dom[0] == "fwd" else bf)[dom[1]]
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    dom_name = {"fwd": "fwd_bf16_kernel<128,%s>" % ("true" if dom[1] else "false"),
+                "bwd": "fa_bwd %s (bwd_pre + bwd_main_kernel<128> + bwd_post)" % ("causal" if dom[1] else "non-causal")}[dom[0]]
+    del q, k, v, do, o, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
 
     if not args.no_extra:
@@ -246,8 +263,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.Hq, "N": w.Nq, "d": w.d,
-                   "masks": ["none", "causal"], "step": "fa_fwd without + with causal mask"},
-        "roofline": {"kernel": "fwd_bf16_kernel<128,false>", "bound": "mfma", "achieved": round(achieved, 2),
+                   "masks": ["none", "causal"], "step": "fa_fwd + fa_bwd, without and with the causal mask"},
+        "roofline": {"kernel": dom_name, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": None},
         "results": results,

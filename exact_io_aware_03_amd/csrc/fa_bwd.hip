@@ -28,8 +28,9 @@
 namespace fa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
+constexpr int kThreads = 256;             // pre / post kernels
+constexpr int kMainThreads = 512;         // main kernel: 8 waves, two per SIMD
+constexpr int kWaves = kMainThreads / 64;
 constexpr int BK = kBwdKeys;  // 128 keys per workgroup
 constexpr int BQ = kBwdRows;  // 64 query rows per step
 
@@ -51,20 +52,24 @@ __device__ __forceinline__ int ds_swz(int row) { return (row >> 1) & 7; }
 template <int D>
 struct BwdLds {
   static constexpr int ROW = D * 2;
-  static constexpr int KT = BK * ROW;    // K, row-major [key][d]
-  static constexpr int QT = BQ * ROW;    // one Q or dO tile, row-major [q][d]
+  static constexpr int KT = BK * ROW;      // K or V, row-major [key][d]
+  static constexpr int QT = BQ * ROW;      // one Q or dO tile, row-major [q][d]
   static constexpr int DST = BK * BQ * 2;  // dS^T, [key][q]
   static constexpr int OFF_K = 0;
-  static constexpr int OFF_Q = OFF_K + KT;         // Q[2]
-  static constexpr int OFF_DO = OFF_Q + 2 * QT;    // dO[2]
+  static constexpr int OFF_V = OFF_K + KT;
+  static constexpr int OFF_Q = OFF_V + KT;          // Q[2]
+  static constexpr int OFF_DO = OFF_Q + 2 * QT;     // dO[2]
   static constexpr int OFF_DS = OFF_DO + 2 * QT;
-  static constexpr int OFF_L = OFF_DS + DST;       // L[2][BQ] fp32 (natural log)
+  static constexpr int OFF_L = OFF_DS + DST;        // L[2][BQ] fp32 (natural log)
   static constexpr int OFF_D = OFF_L + 2 * BQ * 4;  // D[2][BQ] fp32
   static constexpr int BYTES = OFF_D + 2 * BQ * 4;
-  static constexpr int RR = 1024 / ROW;            // rows per 1 KiB direct-to-LDS load
-  static constexpr int QDMA = QT / 1024 / kWaves;  // loads per wave per Q or dO tile
-  static constexpr int KDMA = KT / 1024 / kWaves;  // loads per wave for the K tile
-  static constexpr int STEP_DMA = 2 * QDMA + 2;    // Q, dO, L, D
+  static constexpr int RR = 1024 / ROW;             // rows per 1 KiB direct-to-LDS load
+  static constexpr int QDMA = QT / 1024 / kWaves;   // loads per wave per Q or dO tile
+  static constexpr int KDMA = KT / 1024 / kWaves;   // loads per wave per K or V tile
+  static constexpr int STEP_DMA = 2 * QDMA + 1;     // Q, dO and one of L (waves 0-3) or D (4-7)
+  // fp32 dK/dV partials of the query-half-1 waves, reduced at the end through LDS
+  static constexpr int RED = (kWaves / 2) * 2 * (D / 32) * 16 * 64 * 4;
+  static_assert(RED <= BYTES, "reduction buffer");
 };
 
 // Raw buffer resource as four scalar words (base, stride 0, size, 32-bit untyped format).
@@ -182,19 +187,23 @@ __global__ __launch_bounds__(kThreads) void bwd_post_kernel(BwdArgs a, long n) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(BwdArgs a) {
   using L = BwdLds<D>;
   constexpr int KS = D / 16, DB = D / 32;
-  constexpr int TILES = 2 * DB / kWaves;  // 32x32 dQ tiles per wave
-  constexpr int NA = TILES * 16;          // dQ atomic instructions per wave and full step
+  constexpr int NT = 2 * DB;        // 32x32 dQ tiles per step (one per wave while they last)
+  constexpr int NA = 16;            // dQ atomic instructions per tile
   static_assert(NA + L::STEP_DMA < 64, "vmcnt range");
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
   char* kl = smem + L::OFF_K;
+  char* vl = smem + L::OFF_V;
   char* dsl = smem + L::OFF_DS;
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int h = lane >> 5, l32 = lane & 31;
+  const int slice = wave & 3;   // 32-key slice of the block
+  const int qhalf = wave >> 2;  // 32-row half of each 64-row query block
+  const bool dq_tile = wave < NT;
   // causal: kv block 0 sees every query block; dispatch order is longest first over all
   // (batch, kv head) pairs. Non-causal: XCD-contiguous ranges of one (batch, kv head).
   int bhk, j;
@@ -209,27 +218,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   }
   const int b = bhk / a.Hkv, hk = bhk % a.Hkv;
   const int kv0 = j * BK;
-  const int kw0 = kv0 + wave * 32;  // this wave's keys
-  const int key = kw0 + l32;        // this lane's key
+  const int kw0 = kv0 + slice * 32;  // this wave's keys
+  const int key = kw0 + l32;         // this lane's key
   const uint16_t* kp = (const uint16_t*)a.k + (long)b * a.Nk * a.k_row + hk * D;
   const uint16_t* vp = (const uint16_t*)a.v + (long)b * a.Nk * a.k_row + hk * D;
 
-  // K, V rows as B operands of S = Q K^T and dP = dO V^T: lane holds key, dims [16ks+8h, +8)
-  bf16x8 kf[KS], vf[KS];
-  {
-    const long valid = ((long)(a.Nk - 1) * a.k_row + D) * 2;
-    const rsrc_t rk = make_rsrc(kp, valid), rv = make_rsrc(vp, valid);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int off = (int)(((long)key * a.k_row + ks * 16 + h * 8) * 2);
-      kf[ks] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
-      vf[ks] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
-    }
-  }
-  // the compiler does not count the asm loads below: its own loads complete first
-  __builtin_amdgcn_s_waitcnt(0);
-  // K rows of the whole block, row-major, for the dQ product
+  // K and V rows of the block, row-major in LDS: B operands of S = Q K^T and dP = dO V^T
+  // (row reads) and of dQ = dS K (transposed reads)
   dma_rows<D, L::KDMA>(kl, kp + (long)kv0 * a.k_row, a.k_row, a.Nk - kv0);
+  dma_rows<D, L::KDMA>(vl, vp + (long)kv0 * a.k_row, a.k_row, a.Nk - kv0);
 
   f32x16 dk[DB], dv[DB];
 #pragma unroll
@@ -243,7 +240,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   const int n_steps = a.G * per_head;
 
   // Issue the loads of step st (query head hk*G + st/per_head, block qb_first + st%per_head)
-  // into buffer st&1: Q and dO tiles, then L and D (one 4-byte load per lane each).
+  // into buffer st&1: Q and dO tiles, and L (waves 0-3) or D (waves 4-7).
   auto issue_step = [&](int st) {
     const int hq = hk * a.G + st / per_head, q0 = (qb_first + st % per_head) * BQ;
     const int buf = st & 1;
@@ -252,23 +249,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
     dma_rows<D, L::QDMA>(smem + L::OFF_DO + buf * L::QT, (const uint16_t*)a.dout + qoff, a.q_row, a.Nq - q0);
     const long loff = ((long)b * a.Hq + hq) * a.Nq + q0;
     const long lbytes = (long)min(BQ, a.Nq - q0) * 4;
-    lds_dma4(dma_rsrc(a.lse + loff, lbytes), smem + L::OFF_L + buf * BQ * 4, lane * 4);
-    lds_dma4(dma_rsrc(a.dvec + loff, lbytes), smem + L::OFF_D + buf * BQ * 4, lane * 4);
+    if (qhalf == 0) lds_dma4(dma_rsrc(a.lse + loff, lbytes), smem + L::OFF_L + buf * BQ * 4, lane * 4);
+    else lds_dma4(dma_rsrc(a.dvec + loff, lbytes), smem + L::OFF_D + buf * BQ * 4, lane * 4);
   };
 
   issue_step(0);
-  bool prev_full = true;  // the previous step issued all NA dQ atomics
+  bool prev_full = true;  // the previous step issued all of this wave's dQ atomics
   for (int st = 0; st < n_steps; ++st) {
     const int hq = hk * a.G + st / per_head, q0 = (qb_first + st % per_head) * BQ;
     const bool has_next = st + 1 < n_steps;
     if (has_next) issue_step(st + 1);
-    // This step's loads are complete once at most the loads issued after them are pending:
-    // the previous step's dQ atomics (when it issued all of them) and the next step's tiles.
+    // This step's loads (and, at st = 0, the K/V tiles) are complete once at most the loads
+    // issued after them are pending: the previous step's dQ atomics (when this wave issued
+    // all of them) and the next step's tiles.
+    const bool after_atomics = st > 0 && prev_full && dq_tile;
     if (has_next) {
-      if (st > 0 && prev_full) wait_vm_barrier<NA + L::STEP_DMA>();
+      if (after_atomics) wait_vm_barrier<NA + L::STEP_DMA>();
       else wait_vm_barrier<L::STEP_DMA>();
     } else {
-      if (st > 0 && prev_full) wait_vm_barrier<NA>();
+      if (after_atomics) wait_vm_barrier<NA>();
       else wait_vm_barrier<0>();
     }
     // LDS addresses are recomputed each step from a pinned copy of the lane index instead of
@@ -282,72 +281,74 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
     const float* lls = (const float*)(smem + L::OFF_L + buf * BQ * 4);
     const float* dls = (const float*)(smem + L::OFF_D + buf * BQ * 4);
 
+    // ---- S = Q K^T and dP = dO V^T for this wave's 32 rows x 32 keys ----
     // (causal blocks entirely above this wave's keys run too: their P is masked to zero)
-    // ---- S = Q K^T and dP = dO V^T for 64 rows x this wave's 32 keys ----
-    f32x16 s[2], g[2];
-#pragma unroll
-    for (int qh = 0; qh < 2; ++qh) {
-      zero16(s[qh]);
-      zero16(g[qh]);
-      const int row = 32 * qh + swap_bits23(ll);
+    f32x16 s, g;
+    zero16(s);
+    zero16(g);
+    {
+      const int row = 32 * qhalf + swap_bits23(ll);  // A operand rows (relabelled)
       const int sw = t_swz<D>(row);
+      const int kr = 32 * slice + ll;                // B operand: this lane's key row
+      const int ksw = t_swz<D>(kr);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int off = row * L::ROW + (((2 * ks + lh) ^ sw) << 4);
-        s[qh] = mfma_32x32x16(*(const bf16x8*)(ql + off), kf[ks], s[qh]);
-        g[qh] = mfma_32x32x16(*(const bf16x8*)(dol + off), vf[ks], g[qh]);
-      }
-      fence();  // bounds the operand reads in flight (register budget)
-    }
-    // register i of half qh holds query row 32qh + (i&7) + 8h + 16(i>>3) and key `key`
-#pragma unroll
-    for (int qh = 0; qh < 2; ++qh) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = 32 * qh + (i & 7) + 8 * h + 16 * (i >> 3);
-        float p = fast_exp2(fmaf(s[qh][i], a.c, -lls[r] * kLog2e));
-        if (key >= a.Nk || (a.causal && key > q0 + r)) p = 0.f;
-        s[qh][i] = p;                         // P
-        g[qh][i] = p * (g[qh][i] - dls[r]);  // dS
+        const int koff = kr * L::ROW + (((2 * ks + lh) ^ ksw) << 4);
+        s = mfma_32x32x16(*(const bf16x8*)(ql + off), *(const bf16x8*)(kl + koff), s);
+        g = mfma_32x32x16(*(const bf16x8*)(dol + off), *(const bf16x8*)(vl + koff), g);
       }
     }
-    // ---- dV += P^T dO, dK += dS^T Q over the 64 rows (16 per step); dS^T to LDS ----
+    // register i holds query row 32qhalf + (i&7) + 8h + 16(i>>3) and key `key`: the 8 rows
+    // (i&7) are consecutive, so L and D come in as 16-byte LDS reads.
+    const int qw0 = q0 + 32 * qhalf;  // first row of this wave's half
+    const bool need_mask = kw0 + 31 >= a.Nk || (a.causal && kw0 + 31 > qw0);
 #pragma unroll
-    for (int kq = 0; kq < BQ / 16; ++kq) {
-      const int e = (kq & 1) * 8;
-      const f32x16& ps = s[kq >> 1];
-      const f32x16& gs = g[kq >> 1];
+    for (int hi = 0; hi < 2; ++hi) {
+      const int r0 = 32 * qhalf + 16 * hi + 8 * lh;
+      const f32x4 la = *(const f32x4*)(lls + r0), lb = *(const f32x4*)(lls + r0 + 4);
+      const f32x4 da = *(const f32x4*)(dls + r0), dbv = *(const f32x4*)(dls + r0 + 4);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const int i = 8 * hi + x;
+        const float lv = x < 4 ? la[x] : lb[x - 4], dvv = x < 4 ? da[x] : dbv[x - 4];
+        float p = fast_exp2(fmaf(s[i], a.c, -lv * kLog2e));
+        if (need_mask && (key >= a.Nk || (a.causal && key > q0 + r0 + x))) p = 0.f;
+        s[i] = p;                   // P
+        g[i] = p * (g[i] - dvv);  // dS
+      }
+    }
+    // ---- dV += P^T dO, dK += dS^T Q over this wave's 32 rows (16 per step); dS^T to LDS ----
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int kq = 2 * qhalf + kk;  // 16-row step within the 64-row block
+      const int e = kk * 8;
       u32x4 pw, gw;
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        pw[x] = pack_bf16x2(ps[e + 2 * x], ps[e + 2 * x + 1]);
-        gw[x] = pack_bf16x2(gs[e + 2 * x], gs[e + 2 * x + 1]);
+        pw[x] = pack_bf16x2(s[e + 2 * x], s[e + 2 * x + 1]);
+        gw[x] = pack_bf16x2(g[e + 2 * x], g[e + 2 * x + 1]);
       }
-      const int kc = wave * 32 + ll;
+      const int kc = 32 * slice + ll;
       *(u32x4*)(dsl + kc * (BQ * 2) + (((2 * kq + lh) ^ ds_swz(kc)) << 4)) = gw;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         dv[db] = mfma_32x32x16(as_bf16x8(pw), tr_frag<L::ROW>(dol, kq, db, ln, t_swz<D>), dv[db]);
         dk[db] = mfma_32x32x16(as_bf16x8(gw), tr_frag<L::ROW>(ql, kq, db, ln, t_swz<D>), dk[db]);
       }
-      fence();
     }
     lds_barrier();  // dS^T complete
 
-    // ---- dQ[64 x D] += dS[64 x 128] K[128 x D]; tile tt = (query half tt%2, dim block tt/2) ----
+    // ---- dQ[64 x D] += dS[64 x 128] K[128 x D]; wave w owns tile (query half w%2, dims w/2) ----
     const bool full = q0 + BQ <= a.Nq;
-#pragma unroll
-    for (int u = 0; u < TILES; ++u) {
-      const int tt = wave + kWaves * u;
-      const int qh = tt & 1, db = tt >> 1;
+    if (dq_tile) {
+      const int qh = wave & 1, db = wave >> 1;
       f32x16 acc;
       zero16(acc);
 #pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
+      for (int ks = 0; ks < BK / 16; ++ks)
         acc = mfma_32x32x16(tr_frag<BQ * 2>(dsl, ks, qh, ln, ds_swz), tr_frag<L::ROW>(kl, ks, db, ln, t_swz<D>),
                             acc);
-        if (ks % 4 == 3) fence();
-      }
       // register i holds query row 32qh + 8(i/4) + 4h + i%4, dim 32db + l32
       float* dst = a.dq_acc + (((long)b * a.Nq + q0 + 32 * qh + 4 * h) * a.Hq + hq) * D + 32 * db + l32;
       const long rs = (long)a.Hq * D;
@@ -365,18 +366,35 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(0);
 
-  // ---- dK = scale * acc, dV = acc (bf16); register i holds key kw0 + 8(i/4) + 4h + i%4 ----
+  // ---- reduce the two query halves' partials; dK = scale * acc, dV = acc (bf16) ----
+  // register i holds key kw0 + 8(i/4) + 4h + i%4, dim 32db + l32
+  wait_vm_barrier<0>();  // every wave is done with the tiles: the LDS is free
+  float* red = (float*)smem + (size_t)slice * (2 * DB * 16 * 64) + lane;
+  if (qhalf == 1) {
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kk = kw0 + 8 * (i >> 2) + 4 * h + (i & 3);
-      if (kk < a.Nk) {
-        const long off = ((long)b * a.Nk + kk) * a.k_row + hk * D + 32 * db + l32;
-        ((__bf16*)a.dk)[off] = (__bf16)(dk[db][i] * a.scale);
-        ((__bf16*)a.dv)[off] = (__bf16)dv[db][i];
+      for (int i = 0; i < 16; ++i) {
+        red[((2 * db) * 16 + i) * 64] = dk[db][i];
+        red[((2 * db + 1) * 16 + i) * 64] = dv[db][i];
       }
-    }
+  }
+  wait_vm_barrier<0>();
+  if (qhalf == 0) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kk = kw0 + 8 * (i >> 2) + 4 * h + (i & 3);
+        const float dkv = dk[db][i] + red[((2 * db) * 16 + i) * 64];
+        const float dvv = dv[db][i] + red[((2 * db + 1) * 16 + i) * 64];
+        if (kk < a.Nk) {
+          const long off = ((long)b * a.Nk + kk) * a.k_row + hk * D + 32 * db + l32;
+          ((__bf16*)a.dk)[off] = (__bf16)(dkv * a.scale);
+          ((__bf16*)a.dv)[off] = (__bf16)dvv;
+        }
+      }
+  }
 }
 
 template <int D>
@@ -385,7 +403,7 @@ hipError_t launch_d(const BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((rows + 3) / 4), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_main_kernel<D>), dim3(a.n_tasks), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((bwd_main_kernel<D>), dim3(a.n_tasks), dim3(kMainThreads), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long n = rows * D;
