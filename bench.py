@@ -190,7 +190,7 @@ def main():
     dom_flops = (ff if dom[0] == "fwd" else bf)[dom[1]]
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
     dom_name = {"fwd": "fwd_bf16_kernel<128,%s>" % ("true" if dom[1] else "false"),
-                "bwd": "fa_bwd %s (bwd_pre + bwd_main_kernel<128> + bwd_post)" % ("causal" if dom[1] else "non-causal")}[dom[0]]
+                "bwd": "fa_bwd %s (bwd_pre + bwd_main_kernel<128> + bwd_dq_kernel<128>)" % ("causal" if dom[1] else "non-causal")}[dom[0]]
     del q, k, v, do, o, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
 

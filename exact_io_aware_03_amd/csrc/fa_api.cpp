@@ -82,8 +82,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
 
 size_t fa_bwd_workspace_size(int B, int Hq, int Nq, int d) {
   if (B < 1 || Hq < 1 || Nq < 1 || d < 1) return 0;
-  const size_t rows = (size_t)B * Hq * Nq;
-  return align256(rows * sizeof(float)) + rows * (size_t)d * sizeof(float);
+  return align256((size_t)B * Hq * Nq * sizeof(float));  // D = rowsum(dO * O)
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
@@ -104,7 +103,6 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.dvec = (float*)workspace;
-  a.dq_acc = (float*)((char*)workspace + align256((size_t)B * Hq * Nq * sizeof(float)));
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.G = Hq / Hkv;
   a.q_row = (long)Hq * d;
   a.k_row = (long)Hkv * d;
@@ -112,9 +110,11 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   a.c = scale * 1.4426950408889634f;
   a.causal = causal ? 1 : 0;
   a.n_kvblk = (Nk + fa::kBwdKeys - 1) / fa::kBwdKeys;
-  const long tasks = (long)B * Hkv * a.n_kvblk;
-  if (tasks > INT_MAX || (long)B * Nq * Hq > INT_MAX / 4) return FA_ERR_INVALID_ARG;
+  a.n_qblk_dq = (Nq + fa::kBwdDqRows - 1) / fa::kBwdDqRows;
+  const long tasks = (long)B * Hkv * a.n_kvblk, tasks_dq = (long)B * Hq * a.n_qblk_dq;
+  if (tasks > INT_MAX || tasks_dq > INT_MAX || (long)B * Nq * Hq > INT_MAX / 4) return FA_ERR_INVALID_ARG;
   a.n_tasks = (int)tasks;
+  a.n_tasks_dq = (int)tasks_dq;
   return hip_status(fa::launch_bwd(a, d, (hipStream_t)stream));
 }
 

@@ -3,25 +3,24 @@
 // Method (Lecture 21 notes, CMU 11-868, §2.6 and exercises 4-6): the forward keeps only O and
 // L = m + log l per row. The backward rebuilds each tile's P = exp(scale*S - L), forms
 // dV += P^T dO, dP = dO V^T, dS = P * (dP - D) with D = rowsum(dO * O) computed by a small
-// pre-kernel (sum_k P_ik dP_ik = dO_i . O_i), dK += scale dS^T Q and dQ += scale dS K. The outer
-// loop runs over K/V blocks so dK and dV stay on chip and only dQ is accumulated across
-// workgroups with atomic adds (half the atomics of a query-outer order).
+// pre-kernel (sum_k P_ik dP_ik = dO_i . O_i), dK += scale dS^T Q and dQ += scale dS K.
 //
-// gfx950 mapping: a workgroup owns 128 keys (32 per wave, one wave per SIMD) of one
-// (batch, kv head) and walks the 64-row query blocks that can see them (causal: only blocks at
-// or below the diagonal, longest task first), for every query head of the GQA group, as one
-// flat sequence of steps. Per step:
-//  * Q, dO (row-major) and L, D of the next step stream into the other half of a double
-//    buffer with direct-to-LDS loads while this step computes;
-//  * S = Q K^T and dP = dO V^T come out of the MFMA with one key per lane (K and V rows sit in
-//    registers for the whole task), so P^T and dS^T feed the dV and dK products straight from
-//    the accumulators (query rows relabelled as in the forward); the B operands of those
-//    products (dO and Q with 8 consecutive rows per lane) are read transposed from the same
-//    row-major tiles with ds_read_b64_tr_b16, one XOR swizzle serving both access patterns;
-//  * dS^T goes to LDS with 16-byte stores and comes back transposed as the A operand of
-//    dQ = dS K (K row-major in LDS for the whole task); each wave owns two 32x32 dQ tiles whose
-//    rows map to coalesced fp32 global atomics.
-// Two barriers per step: one after this step's tiles have landed, one after dS^T is complete.
+// gfx950 mapping: two kernels after the pre-kernel, neither with atomics.
+//  * dK/dV, key-block outer: a workgroup owns 128 keys of one (batch, kv head); its eight
+//    waves (two per SIMD) are four 32-key slices x two 32-row halves of every 64-row query
+//    block it walks (causal: only blocks at or below the diagonal, longest task first), for
+//    every query head of the GQA group, as one flat sequence of steps. K and V sit in LDS for
+//    the whole task; each step's Q, dO, L and D stream into the other half of a double buffer
+//    with direct-to-LDS loads while the current step computes. S = Q K^T and dP = dO V^T come
+//    out of the MFMA with one key per lane, so P^T and dS^T feed the dV and dK products
+//    straight from the accumulators (query rows relabelled as in the forward); the B operands
+//    (dO and Q, 8 consecutive rows per lane) are read transposed from the same row-major tiles
+//    with ds_read_b64_tr_b16, one XOR swizzle serving both access patterns. The two row
+//    halves' partial dK/dV are summed through LDS at the end.
+//  * dQ, query-block outer (below): like the forward, with dQ in registers.
+// Recomputing S and dP in the dQ kernel costs two extra products per tile; in exchange dQ is
+// never read back and rewritten through fp32 atomics (one pass over an fp32 copy of dQ per key
+// block), and the result is reproducible.
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -46,21 +45,17 @@ template <int D>
 __device__ __forceinline__ int t_swz(int row) {
   return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((row >> 1) & 7);
 }
-// dS^T tile [key][query], 128-byte rows.
-__device__ __forceinline__ int ds_swz(int row) { return (row >> 1) & 7; }
 
 template <int D>
 struct BwdLds {
   static constexpr int ROW = D * 2;
   static constexpr int KT = BK * ROW;      // K or V, row-major [key][d]
   static constexpr int QT = BQ * ROW;      // one Q or dO tile, row-major [q][d]
-  static constexpr int DST = BK * BQ * 2;  // dS^T, [key][q]
   static constexpr int OFF_K = 0;
   static constexpr int OFF_V = OFF_K + KT;
   static constexpr int OFF_Q = OFF_V + KT;          // Q[2]
   static constexpr int OFF_DO = OFF_Q + 2 * QT;     // dO[2]
-  static constexpr int OFF_DS = OFF_DO + 2 * QT;
-  static constexpr int OFF_L = OFF_DS + DST;        // L[2][BQ] fp32 (natural log)
+  static constexpr int OFF_L = OFF_DO + 2 * QT;     // L[2][BQ] fp32 (natural log)
   static constexpr int OFF_D = OFF_L + 2 * BQ * 4;  // D[2][BQ] fp32
   static constexpr int BYTES = OFF_D + 2 * BQ * 4;
   static constexpr int RR = 1024 / ROW;             // rows per 1 KiB direct-to-LDS load
@@ -158,7 +153,7 @@ __device__ __forceinline__ bf16x8 tr_frag(const char* base, int ks, int cb, int 
   return __builtin_bit_cast(bf16x8, c);
 }
 
-// D = rowsum(dO * O) per (batch, head, row) and a zeroed fp32 dQ accumulator. One wave per row.
+// D = rowsum(dO * O) per (batch, head, row). One wave per row.
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // (b*Nq + i)*Hq + h
@@ -176,34 +171,22 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
   if (lane == 0) a.dvec[((long)b * a.Hq + h) * a.Nq + i] = s;
-  float* acc = a.dq_acc + (long)row * D;
-  for (int e = lane; e < D; e += 64) acc[e] = 0.f;
-}
-
-template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_post_kernel(BwdArgs a, long n) {
-  for (long e = (long)blockIdx.x * kThreads + threadIdx.x; e < n; e += (long)gridDim.x * kThreads)
-    ((__bf16*)a.dq)[e] = (__bf16)(a.dq_acc[e] * a.scale);
 }
 
 template <int D>
 __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(BwdArgs a) {
   using L = BwdLds<D>;
   constexpr int KS = D / 16, DB = D / 32;
-  constexpr int NT = 2 * DB;        // 32x32 dQ tiles per step (one per wave while they last)
-  constexpr int NA = 16;            // dQ atomic instructions per tile
-  static_assert(NA + L::STEP_DMA < 64, "vmcnt range");
+  static_assert(L::STEP_DMA < 64, "vmcnt range");
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
   char* kl = smem + L::OFF_K;
   char* vl = smem + L::OFF_V;
-  char* dsl = smem + L::OFF_DS;
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int h = lane >> 5, l32 = lane & 31;
   const int slice = wave & 3;   // 32-key slice of the block
   const int qhalf = wave >> 2;  // 32-row half of each 64-row query block
-  const bool dq_tile = wave < NT;
   // causal: kv block 0 sees every query block; dispatch order is longest first over all
   // (batch, kv head) pairs. Non-causal: XCD-contiguous ranges of one (batch, kv head).
   int bhk, j;
@@ -254,22 +237,12 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(BwdArgs a) {
   };
 
   issue_step(0);
-  bool prev_full = true;  // the previous step issued all of this wave's dQ atomics
   for (int st = 0; st < n_steps; ++st) {
-    const int hq = hk * a.G + st / per_head, q0 = (qb_first + st % per_head) * BQ;
-    const bool has_next = st + 1 < n_steps;
-    if (has_next) issue_step(st + 1);
-    // This step's loads (and, at st = 0, the K/V tiles) are complete once at most the loads
-    // issued after them are pending: the previous step's dQ atomics (when this wave issued
-    // all of them) and the next step's tiles.
-    const bool after_atomics = st > 0 && prev_full && dq_tile;
-    if (has_next) {
-      if (after_atomics) wait_vm_barrier<NA + L::STEP_DMA>();
-      else wait_vm_barrier<L::STEP_DMA>();
-    } else {
-      if (after_atomics) wait_vm_barrier<NA>();
-      else wait_vm_barrier<0>();
-    }
+    const int q0 = (qb_first + st % per_head) * BQ;
+    // This step's loads (and, at st = 0, the K/V tiles) have landed, and every wave is done
+    // with the previous step, whose buffer the next step's loads refill: issue them only now.
+    wait_vm_barrier<0>();
+    if (st + 1 < n_steps) issue_step(st + 1);
     // LDS addresses are recomputed each step from a pinned copy of the lane index instead of
     // being hoisted out of the loop: VALU time is cheap here, registers are not.
     int ln = lane;
@@ -318,7 +291,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(BwdArgs a) {
         g[i] = p * (g[i] - dvv);  // dS
       }
     }
-    // ---- dV += P^T dO, dK += dS^T Q over this wave's 32 rows (16 per step); dS^T to LDS ----
+    // ---- dV += P^T dO, dK += dS^T Q over this wave's 32 rows (16 per step) ----
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int kq = 2 * qhalf + kk;  // 16-row step within the 64-row block
@@ -329,40 +302,12 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(BwdArgs a) {
         pw[x] = pack_bf16x2(s[e + 2 * x], s[e + 2 * x + 1]);
         gw[x] = pack_bf16x2(g[e + 2 * x], g[e + 2 * x + 1]);
       }
-      const int kc = 32 * slice + ll;
-      *(u32x4*)(dsl + kc * (BQ * 2) + (((2 * kq + lh) ^ ds_swz(kc)) << 4)) = gw;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         dv[db] = mfma_32x32x16(as_bf16x8(pw), tr_frag<L::ROW>(dol, kq, db, ln, t_swz<D>), dv[db]);
         dk[db] = mfma_32x32x16(as_bf16x8(gw), tr_frag<L::ROW>(ql, kq, db, ln, t_swz<D>), dk[db]);
       }
     }
-    lds_barrier();  // dS^T complete
-
-    // ---- dQ[64 x D] += dS[64 x 128] K[128 x D]; wave w owns tile (query half w%2, dims w/2) ----
-    const bool full = q0 + BQ <= a.Nq;
-    if (dq_tile) {
-      const int qh = wave & 1, db = wave >> 1;
-      f32x16 acc;
-      zero16(acc);
-#pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks)
-        acc = mfma_32x32x16(tr_frag<BQ * 2>(dsl, ks, qh, ln, ds_swz), tr_frag<L::ROW>(kl, ks, db, ln, t_swz<D>),
-                            acc);
-      // register i holds query row 32qh + 8(i/4) + 4h + i%4, dim 32db + l32
-      float* dst = a.dq_acc + (((long)b * a.Nq + q0 + 32 * qh + 4 * h) * a.Hq + hq) * D + 32 * db + l32;
-      const long rs = (long)a.Hq * D;
-      if (full) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) unsafeAtomicAdd(dst + (8 * (i >> 2) + (i & 3)) * rs, acc[i]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (q0 + 32 * qh + 8 * (i >> 2) + 4 * h + (i & 3) < a.Nq)
-            unsafeAtomicAdd(dst + (8 * (i >> 2) + (i & 3)) * rs, acc[i]);
-      }
-    }
-    prev_full = full;
   }
   __builtin_amdgcn_s_waitcnt(0);
 
@@ -397,6 +342,172 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(BwdArgs a) {
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// dQ = scale * dS K, query-block outer (no atomics): each wave owns 32 query rows and keeps
+// Q, dO, L and D of its rows in registers while 64-key K/V tiles stream through a four-buffer
+// LDS ring (direct-to-LDS loads three tiles ahead). Per tile, as in the forward, the products
+// come out transposed with one query per lane: S^T = K Q^T and dP^T = V dO^T (K and V rows
+// relabelled so each lane half holds 8 consecutive keys), then P = exp(scale*S - L) and
+// dS = P * (dP - D) are per-lane scalar work, and dS^T goes from the accumulator straight into
+// the B operand of dQ^T += K^T dS^T, K^T read transposed from the same K tile.
+constexpr int DQ_BR = kBwdDqRows;  // 256 query rows per workgroup
+constexpr int DQ_BC = kBwdDqKeys;  // 64 keys per tile
+constexpr int DQ_NBUF = 4;
+
+template <int D>
+struct DqTile {
+  static constexpr int ROW = D * 2;
+  static constexpr int T_BYTES = DQ_BC * ROW;              // K or V tile
+  static constexpr int BUF = 2 * T_BYTES;                  // K then V
+  static constexpr int RR = 1024 / ROW;                    // rows per 1 KiB load
+  static constexpr int DMA = T_BYTES / 1024 / kWaves;      // loads per wave per tensor per tile
+  static constexpr int VMCNT = 2 * DMA;                    // loads per wave per tile
+};
+
+// This wave's share of the direct-to-LDS loads of the K and V tile starting at key kv0.
+template <int D>
+__device__ __forceinline__ void dq_dma_tile(char* buf, const uint16_t* kp, const uint16_t* vp, long k_row, int kv0,
+                                            int nk) {
+  using T = DqTile<D>;
+  dma_rows<D, T::DMA>(buf, kp + (long)kv0 * k_row, k_row, nk - kv0);
+  dma_rows<D, T::DMA>(buf + T::T_BYTES, vp + (long)kv0 * k_row, k_row, nk - kv0);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kMainThreads, 1) void bwd_dq_kernel(BwdArgs a) {
+  using T = DqTile<D>;
+  constexpr int KS = D / 16, DB = D / 32;
+  static_assert(3 * T::VMCNT < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) char smem[DQ_NBUF * T::BUF];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5, l32 = lane & 31;
+  int bh, qb;
+  if (CAUSAL) {  // longest first over all heads
+    const int n_bh = a.n_tasks_dq / a.n_qblk_dq;
+    qb = a.n_qblk_dq - 1 - (int)blockIdx.x / n_bh;
+    bh = (int)blockIdx.x % n_bh;
+  } else {
+    const int task = xcd_contiguous_task(blockIdx.x, a.n_tasks_dq);
+    bh = task / a.n_qblk_dq;
+    qb = task % a.n_qblk_dq;
+  }
+  const int b = bh / a.Hq, hq = bh % a.Hq, hk = hq / a.G;
+  const long qbase = (long)b * a.Nq * a.q_row + hq * D;
+  const uint16_t* kp = (const uint16_t*)a.k + (long)b * a.Nk * a.k_row + hk * D;
+  const uint16_t* vp = (const uint16_t*)a.v + (long)b * a.Nk * a.k_row + hk * D;
+  const long q_valid = ((long)(a.Nq - 1) * a.q_row + D) * 2;
+
+  // rows interleaved over the waves so a causal block's work is even across them
+  const int q0 = qb * DQ_BR + 32 * wave;
+  const int qi = q0 + l32;  // this lane's query row
+  // Q and dO as B operands of S^T = K Q^T and dP^T = V dO^T: column qi, dims [16ks + 8h, +8)
+  bf16x8 qf[KS], gf[KS];
+  {
+    const rsrc_t rq = make_rsrc((const uint16_t*)a.q + qbase, q_valid);
+    const rsrc_t rg = make_rsrc((const uint16_t*)a.dout + qbase, q_valid);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int off = (int)(((long)qi * a.q_row + ks * 16 + h * 8) * 2);
+      qf[ks] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+      gf[ks] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(rg, off, 0, 0));
+    }
+  }
+  float l2 = 0.f, dd = 0.f;  // L in base 2 and D of row qi (rows past Nq contribute nothing)
+  if (qi < a.Nq) {
+    l2 = a.lse[((long)b * a.Hq + hq) * a.Nq + qi] * kLog2e;
+    dd = a.dvec[((long)b * a.Hq + hq) * a.Nq + qi];
+  }
+
+  int n_tiles = (a.Nk + DQ_BC - 1) / DQ_BC;
+  int last_w = n_tiles - 1;
+  if (CAUSAL) {
+    n_tiles = min(n_tiles, (min(a.Nq, (qb + 1) * DQ_BR) - 1) / DQ_BC + 1);
+    last_w = min(n_tiles - 1, (q0 + 31) / DQ_BC);
+  }
+  const int nk_load = min(a.Nk, n_tiles * DQ_BC);
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) zero16(acc[db]);
+
+  // the compiler does not count the asm loads below: its own loads complete first
+  __builtin_amdgcn_s_waitcnt(0);
+  dq_dma_tile<D>(smem, kp, vp, a.k_row, 0, nk_load);
+  dq_dma_tile<D>(smem + T::BUF, kp, vp, a.k_row, DQ_BC, nk_load);
+  dq_dma_tile<D>(smem + 2 * T::BUF, kp, vp, a.k_row, 2 * DQ_BC, nk_load);
+
+  for (int j = 0; j < n_tiles; ++j) {
+    // tile j landed (tiles j+1 and j+2 may be pending); every wave is done with tile j-1,
+    // whose buffer the prefetch of tile j+3 refills
+    wait_vm_barrier<2 * T::VMCNT>();
+    dq_dma_tile<D>(smem + ((j + 3) % DQ_NBUF) * T::BUF, kp, vp, a.k_row, (j + 3) * DQ_BC, nk_load);
+    if (j > last_w) continue;
+    const char* kt = smem + (j % DQ_NBUF) * T::BUF;
+    const char* vt = kt + T::T_BYTES;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int lh = ln >> 5, ll = ln & 31;
+    const int kv0 = j * DQ_BC;
+
+    // ---- S^T and dP^T for 64 keys (two 32-key blocks) x this wave's 32 queries ----
+    f32x16 s[2], g[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      zero16(s[kb]);
+      zero16(g[kb]);
+      const int row = 32 * kb + swap_bits23(ll);
+      const int sw = t_swz<D>(row);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int off = row * T::ROW + (((2 * ks + lh) ^ sw) << 4);
+        s[kb] = mfma_32x32x16(*(const bf16x8*)(kt + off), qf[ks], s[kb]);
+        g[kb] = mfma_32x32x16(*(const bf16x8*)(vt + off), gf[ks], g[kb]);
+      }
+      fence();  // bounds the K/V fragments in flight (register budget)
+    }
+    // register i of block kb holds key kv0 + 32kb + (i&7) + 8h + 16(i>>3), query qi
+    const bool need_mask = kv0 + DQ_BC > a.Nk || (CAUSAL && kv0 + DQ_BC - 1 > q0);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float p = fast_exp2(fmaf(s[kb][i], a.c, -l2));
+        if (need_mask) {
+          const int key = kv0 + 32 * kb + (i & 7) + 8 * h + 16 * (i >> 3);
+          if (key >= a.Nk || (CAUSAL && key > qi)) p = 0.f;
+        }
+        g[kb][i] = p * (g[kb][i] - dd);  // dS
+      }
+    // ---- dQ^T += K^T dS^T: 16-key step kk takes dS registers 8(kk&1) .. +7 of block kk/2 ----
+#pragma unroll
+    for (int kk = 0; kk < DQ_BC / 16; ++kk) {
+      const f32x16& gs = g[kk >> 1];
+      const int e = (kk & 1) * 8;
+      u32x4 gw;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) gw[x] = pack_bf16x2(gs[e + 2 * x], gs[e + 2 * x + 1]);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        acc[db] = mfma_32x32x16(tr_frag<T::ROW>(kt, kk, db, ln, t_swz<D>), as_bf16x8(gw), acc[db]);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // drain the tail prefetches before the workgroup ends
+
+  // ---- dQ = scale * acc (bf16); register i of acc[db] is dim 32db + 8(i/4) + 4h + i%4 ----
+  const rsrc_t rdq = make_rsrc((uint16_t*)a.dq + qbase, q_valid);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      u32x2 w;
+      w[0] = pack_bf16x2(acc[db][4 * jj + 0] * a.scale, acc[db][4 * jj + 1] * a.scale);
+      w[1] = pack_bf16x2(acc[db][4 * jj + 2] * a.scale, acc[db][4 * jj + 3] * a.scale);
+      __builtin_amdgcn_raw_buffer_store_b64(w, rdq, (int)(((long)qi * a.q_row + 32 * db + 8 * jj + 4 * h) * 2), 0, 0);
+    }
+}
+
 template <int D>
 hipError_t launch_d(const BwdArgs& a, hipStream_t s) {
   const long rows = (long)a.B * a.Nq * a.Hq;
@@ -406,9 +517,8 @@ hipError_t launch_d(const BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((bwd_main_kernel<D>), dim3(a.n_tasks), dim3(kMainThreads), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const long n = rows * D;
-  const long blocks = (n + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL((bwd_post_kernel<D>), dim3(blocks < 65536 ? blocks : 65536), dim3(kThreads), 0, s, a, n);
+  if (a.causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3(a.n_tasks_dq), dim3(kMainThreads), 0, s, a);
+  else hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3(a.n_tasks_dq), dim3(kMainThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -49,14 +49,15 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* dvec;    // D = rowsum(dO * O), [B, Hq, Nq]
-  float* dq_acc;  // fp32 dQ accumulator, [B, Nq, Hq, d]
   int B, Hq, Hkv, Nq, Nk, G;
   long q_row, k_row;
   float scale;
   float c;
   int causal;
   int n_kvblk;
-  int n_tasks;
+  int n_tasks;     // dK/dV kernel: B * Hkv * n_kvblk
+  int n_qblk_dq;   // dQ kernel: query blocks per (batch, head)
+  int n_tasks_dq;  // B * Hq * n_qblk_dq
 };
 
 // Planner constants shared by the host code and the kernels.
@@ -65,8 +66,10 @@ constexpr int kFwdF32Rows = 128;  // query rows per fp32 forward workgroup (4 wa
 constexpr int kFwdKeys = 64;      // keys per forward K/V tile
 constexpr int kFwdF32Keys = 32;   // keys per tile in the fp32 forward
 constexpr int kDecMinChunk = 256; // smallest decode chunk (4 waves x 64 keys)
-constexpr int kBwdKeys = 128;     // keys per backward workgroup (4 waves x 32)
-constexpr int kBwdRows = 64;      // query rows per backward inner step
+constexpr int kBwdKeys = 128;     // keys per dK/dV workgroup (4 key slices x 32)
+constexpr int kBwdRows = 64;      // query rows per dK/dV inner step
+constexpr int kBwdDqRows = 256;   // query rows per dQ workgroup (8 waves x 32)
+constexpr int kBwdDqKeys = 64;    // keys per dQ K/V tile
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, hipStream_t s);

@@ -62,7 +62,7 @@ enum fa_status {
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
            int Nq, int Nk, int d, int causal, float scale, int dtype, void* stream);
 
-/* Workspace bytes fa_bwd needs: D (fp32 B*Hq*Nq) and an fp32 dQ accumulator (B*Nq*Hq*d). */
+/* Workspace bytes fa_bwd needs: D = rowsum(dO * O), fp32 [B, Hq, Nq]. */
 size_t fa_bwd_workspace_size(int B, int Hq, int Nq, int d);
 
 /*
@@ -70,8 +70,8 @@ size_t fa_bwd_workspace_size(int B, int Hq, int Nq, int d);
  * P = exp(scale*S - L) is recomputed per tile; dV = P^T dO; dP = dO V^T; dS = P * (dP - D) with
  * D = rowsum(dO * O); dQ = scale * dS K; dK = scale * dS^T Q. For GQA, dK and dV sum over the
  * query heads of a group. dtype FA_BF16 only (fp32 gives FA_ERR_UNSUPPORTED). dq has Q's layout,
- * dk and dv K's. dQ is accumulated with fp32 atomics, so results may differ between runs in the
- * last bits.
+ * dk and dv K's. dK/dV come from a key-block-outer kernel and dQ from a query-block-outer one
+ * (both recompute P), so no atomics are involved and results are reproducible run to run.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
            void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
