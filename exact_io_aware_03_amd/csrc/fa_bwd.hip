@@ -153,24 +153,29 @@ __device__ __forceinline__ bf16x8 tr_frag(const char* base, int ks, int cb, int 
   return __builtin_bit_cast(bf16x8, c);
 }
 
-// D = rowsum(dO * O) per (batch, head, row). One wave per row.
+// D = rowsum(dO * O) per (batch, head, row): D/8 lanes per row, 16 bytes of O and dO each.
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // (b*Nq + i)*Hq + h
-  const int lane = threadIdx.x & 63;
-  if (row >= a.B * a.Nq * a.Hq) return;
-  const int h = row % a.Hq, i = (row / a.Hq) % a.Nq, b = row / (a.Hq * a.Nq);
-  const uint16_t* op = (const uint16_t*)a.o + (long)row * D;
-  const uint16_t* gp = (const uint16_t*)a.dout + (long)row * D;
+  constexpr int LPR = D / 8;  // lanes per row
+  const long row = ((long)blockIdx.x * kThreads + threadIdx.x) / LPR;  // (b*Nq + i)*Hq + h
+  const int sub = threadIdx.x % LPR;
+  const long rows = (long)a.B * a.Nq * a.Hq;
   float s = 0.f;
-  for (int e = lane; e < D / 2; e += 64) {
-    const uint32_t ow = ((const uint32_t*)op)[e], gw = ((const uint32_t*)gp)[e];
-    s = fmaf(bf16_lo(ow), bf16_lo(gw), s);
-    s = fmaf(bf16_hi(ow), bf16_hi(gw), s);
+  if (row < rows) {
+    const u32x4 ow = *(const u32x4*)((const uint16_t*)a.o + row * D + sub * 8);
+    const u32x4 gw = *(const u32x4*)((const uint16_t*)a.dout + row * D + sub * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s = fmaf(bf16_lo(ow[e]), bf16_lo(gw[e]), s);
+      s = fmaf(bf16_hi(ow[e]), bf16_hi(gw[e]), s);
+    }
   }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-  if (lane == 0) a.dvec[((long)b * a.Hq + h) * a.Nq + i] = s;
+  for (int off = LPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  if (row < rows && sub == 0) {
+    const int h = row % a.Hq, i = (row / a.Hq) % a.Nq, b = row / ((long)a.Hq * a.Nq);
+    a.dvec[((long)b * a.Hq + h) * a.Nq + i] = s;
+  }
 }
 
 template <int D>
@@ -187,13 +192,11 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(BwdArgs a) {
   const int h = lane >> 5, l32 = lane & 31;
   const int slice = wave & 3;   // 32-key slice of the block
   const int qhalf = wave >> 2;  // 32-row half of each 64-row query block
-  // causal: kv block 0 sees every query block; dispatch order is longest first over all
-  // (batch, kv head) pairs. Non-causal: XCD-contiguous ranges of one (batch, kv head).
+  // causal: kv block 0 sees every query block; dispatch order is longest first, each XCD
+  // keeping its own (batch, kv head) pairs. Non-causal: XCD-contiguous task ranges.
   int bhk, j;
   if (a.causal) {
-    const int n_bhk = a.n_tasks / a.n_kvblk;
-    j = (int)blockIdx.x / n_bhk;
-    bhk = (int)blockIdx.x % n_bhk;
+    xcd_longest_first((int)blockIdx.x, a.n_tasks / a.n_kvblk, bhk, j);
   } else {
     const int task = xcd_contiguous_task(blockIdx.x, a.n_tasks);
     bhk = task / a.n_kvblk;
@@ -384,10 +387,10 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5, l32 = lane & 31;
   int bh, qb;
-  if (CAUSAL) {  // longest first over all heads
-    const int n_bh = a.n_tasks_dq / a.n_qblk_dq;
-    qb = a.n_qblk_dq - 1 - (int)blockIdx.x / n_bh;
-    bh = (int)blockIdx.x % n_bh;
+  if (CAUSAL) {  // longest first, each XCD keeping its own heads
+    int lvl;
+    xcd_longest_first((int)blockIdx.x, a.n_tasks_dq / a.n_qblk_dq, bh, lvl);
+    qb = a.n_qblk_dq - 1 - lvl;
   } else {
     const int task = xcd_contiguous_task(blockIdx.x, a.n_tasks_dq);
     bh = task / a.n_qblk_dq;
@@ -510,8 +513,9 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 
 template <int D>
 hipError_t launch_d(const BwdArgs& a, hipStream_t s) {
-  const long rows = (long)a.B * a.Nq * a.Hq;
-  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((rows + 3) / 4), dim3(kThreads), 0, s, a);
+  const long rows = (long)a.B * a.Nq * a.Hq, rows_per_block = kThreads / (D / 8);
+  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((rows + rows_per_block - 1) / rows_per_block), dim3(kThreads), 0, s,
+                     a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_main_kernel<D>), dim3(a.n_tasks), dim3(kMainThreads), 0, s, a);

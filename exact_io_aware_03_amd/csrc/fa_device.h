@@ -92,6 +92,22 @@ __device__ __forceinline__ int xcd_contiguous_task(int wg, int n) {
   return x * per + (x < rem ? x : rem) + i;
 }
 
+// Causal task order: block ids dispatch longest task first (level 0 = longest) while every XCD
+// keeps a fixed subset of the n_grp groups (heads), so a group's K/V rows stay under one L2
+// and all XCDs walk the levels together. Falls back to a plain longest-first order when n_grp
+// is not a multiple of 8. Bijective on [0, n_grp * n_lvl).
+__device__ __forceinline__ void xcd_longest_first(int wg, int n_grp, int& grp, int& lvl) {
+  constexpr int kXcd = 8;
+  if (n_grp % kXcd == 0) {
+    const int per = n_grp / kXcd, x = wg % kXcd, i = wg / kXcd;
+    lvl = i / per;
+    grp = x * per + i % per;
+  } else {
+    lvl = wg / n_grp;
+    grp = wg % n_grp;
+  }
+}
+
 // Row relabelling used for the A operand of the score product: swapping bits 2 and 3 of the
 // row index makes accumulator register i of lane half h hold contraction index
 // (i & 7) + 8*h + 16*(i >> 3), i.e. each lane half owns 8 consecutive keys per 16-key step,

@@ -300,13 +300,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5, l32 = lane & 31;
   // Non-causal: every task costs the same; each XCD takes a contiguous run of tasks so the
-  // query blocks of one head share that XCD's L2. Causal: dispatch order is longest first
-  // across all heads (every query block of the last row band, then the next band, ...).
+  // query blocks of one head share that XCD's L2. Causal: longest first (the last row band of
+  // every head, then the next band, ...) with each XCD keeping its own heads.
   int bh, qb;
   if (CAUSAL) {
-    const int n_bh = a.n_tasks / a.n_qblk;
-    qb = a.n_qblk - 1 - (int)blockIdx.x / n_bh;
-    bh = (int)blockIdx.x % n_bh;
+    int lvl;
+    xcd_longest_first((int)blockIdx.x, a.n_tasks / a.n_qblk, bh, lvl);
+    qb = a.n_qblk - 1 - lvl;
   } else {
     const int task = xcd_contiguous_task(blockIdx.x, a.n_tasks);
     bh = task / a.n_qblk;
