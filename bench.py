@@ -79,6 +79,32 @@ def time_launches(fn, reps, warmup):
     return [a.elapsed_time(b) for a, b in evs]
 
 
+def csrc_sha256():
+    import hashlib
+    import glob
+
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "exact_io_aware_03_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(call):
+    """HBM bytes per call of `call` from the committed FETCH_SIZE/WRITE_SIZE summary, or None when
+    the kernel sources changed since those counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_counters.json")
+    try:
+        with open(path) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("csrc_sha256") != csrc_sha256() or call not in rec.get("calls", {}):
+        return None
+    return int(rec["calls"][call]["traffic_bytes"])
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The fp64 oracle, as it stands, on whole heads of the workload until ~budget_s elapse."""
     from oracle import attention as ora
@@ -189,6 +215,7 @@ def main():
     dom_ms = part_ms[dom]
     dom_flops = (ff if dom[0] == "fwd" else bf)[dom[1]]
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    dom_call = "%s %s" % ("fa_fwd" if dom[0] == "fwd" else "fa_bwd", "causal" if dom[1] else "non-causal")
     dom_name = {"fwd": "fwd_bf16_kernel<128,%s>" % ("true" if dom[1] else "false"),
                 "bwd": "fa_bwd %s (bwd_pre + bwd_main_kernel<128> + bwd_dq_kernel<128>)" % ("causal" if dom[1] else "non-causal")}[dom[0]]
     del q, k, v, do, o, lse, dq, dk, dv, ws
@@ -266,7 +293,7 @@ def main():
                    "masks": ["none", "causal"], "step": "fa_fwd + fa_bwd, without and with the causal mask"},
         "roofline": {"kernel": dom_name, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(dom_call)},
         "results": results,
     }
     if not args.no_cpu:

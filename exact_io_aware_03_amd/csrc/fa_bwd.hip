@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(BwdArgs a) {
   // keeping its own (batch, kv head) pairs. Non-causal: XCD-contiguous task ranges.
   int bhk, j;
   if (a.causal) {
-    xcd_longest_first((int)blockIdx.x, a.n_tasks / a.n_kvblk, bhk, j);
+    xcd_longest_first((int)blockIdx.x, a.n_tasks / a.n_kvblk, a.n_kvblk, bhk, j);
   } else {
     const int task = xcd_contiguous_task(blockIdx.x, a.n_tasks);
     bhk = task / a.n_kvblk;
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   int bh, qb;
   if (CAUSAL) {  // longest first, each XCD keeping its own heads
     int lvl;
-    xcd_longest_first((int)blockIdx.x, a.n_tasks_dq / a.n_qblk_dq, bh, lvl);
+    xcd_longest_first((int)blockIdx.x, a.n_tasks_dq / a.n_qblk_dq, a.n_qblk_dq, bh, lvl);
     qb = a.n_qblk_dq - 1 - lvl;
   } else {
     const int task = xcd_contiguous_task(blockIdx.x, a.n_tasks_dq);

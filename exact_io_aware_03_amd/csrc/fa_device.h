@@ -92,16 +92,21 @@ __device__ __forceinline__ int xcd_contiguous_task(int wg, int n) {
   return x * per + (x < rem ? x : rem) + i;
 }
 
-// Causal task order: block ids dispatch longest task first (level 0 = longest) while every XCD
-// keeps a fixed subset of the n_grp groups (heads), so a group's K/V rows stay under one L2
-// and all XCDs walk the levels together. Falls back to a plain longest-first order when n_grp
-// is not a multiple of 8. Bijective on [0, n_grp * n_lvl).
-__device__ __forceinline__ void xcd_longest_first(int wg, int n_grp, int& grp, int& lvl) {
-  constexpr int kXcd = 8;
+// Causal task order over n_grp groups (heads) x n_lvl levels (level 0 = longest task). Every
+// XCD keeps a fixed set of groups and works through them in clusters of `cs` groups, longest
+// level first inside a cluster, with cs * n_lvl about the XCD's 32 compute units: the tasks
+// sharing a group's K/V rows run together under one L2 while the long ones still start first.
+// Falls back to a plain longest-first order when n_grp is not a multiple of 8. Bijective on
+// [0, n_grp * n_lvl).
+__device__ __forceinline__ void xcd_longest_first(int wg, int n_grp, int n_lvl, int& grp, int& lvl) {
+  constexpr int kXcd = 8, kCuPerXcd = 32;
   if (n_grp % kXcd == 0) {
     const int per = n_grp / kXcd, x = wg % kXcd, i = wg / kXcd;
-    lvl = i / per;
-    grp = x * per + i % per;
+    int cs = 1;
+    while (cs * 2 * n_lvl <= kCuPerXcd && per % (cs * 2) == 0) cs *= 2;
+    const int c = i / (cs * n_lvl), r = i % (cs * n_lvl);
+    lvl = r / cs;
+    grp = x * per + c * cs + r % cs;
   } else {
     lvl = wg / n_grp;
     grp = wg % n_grp;

@@ -305,7 +305,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   int bh, qb;
   if (CAUSAL) {
     int lvl;
-    xcd_longest_first((int)blockIdx.x, a.n_tasks / a.n_qblk, bh, lvl);
+    xcd_longest_first((int)blockIdx.x, a.n_tasks / a.n_qblk, a.n_qblk, bh, lvl);
     qb = a.n_qblk - 1 - lvl;
   } else {
     const int task = xcd_contiguous_task(blockIdx.x, a.n_tasks);
