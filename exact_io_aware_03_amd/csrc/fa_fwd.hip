@@ -2,33 +2,34 @@
 //
 // Method (Lecture 21 notes, CMU 11-868: §2.2 online softmax, §2.5 whole-tile causal skip,
 // §3.1 query-block-outer loop, §3.2 deferred normalisation with only L stored, §3.4 split-Q
-// across warps, §4.3 overlap of the softmax with the matrix products; "FlashAttention Tiling
-// 策略与在线 Softmax", §3 tiling): one workgroup owns 256 query rows, each of its four waves 64 of
-// them; K/V tiles of 64 keys stream through LDS while the running max m, running sum l and the
-// output accumulator stay in registers, so the N x N scores never leave the chip.
+// across warps, §4.3 overlap of the softmax with the matrix products, §5.3 conditional
+// rescaling; "FlashAttention Tiling 策略与在线 Softmax", §3 tiling): one workgroup owns 256
+// query rows of one (batch, head), each of its eight waves (two per SIMD) 32 of them; K/V tiles
+// of 64 keys stream through LDS while the running max m, running sum l and the output
+// accumulator stay in registers, so the N x N scores never leave the chip.
 //
 // gfx950 mapping:
 //  * scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16), so every lane
-//    owns one query per 32-row block: the row max and sum are in-lane reductions plus one
-//    v_permlane32_swap, and the rescale factor alpha is a per-lane scalar;
+//    owns one query: the row max and sum are in-lane reductions plus one v_permlane32_swap,
+//    and the rescale factor alpha is a per-lane scalar;
 //  * the K rows fed to the score MFMA are relabelled (bits 2 and 3 of the row swapped), which
 //    leaves each lane half holding 8 consecutive keys per 16-key step: the probabilities go
 //    from the score accumulator straight into the B operand of O^T += V^T P^T, no LDS trip;
-//  * 64 rows per wave: every K/V fragment read from LDS feeds two MFMAs;
-//  * software pipeline inside the wave: the score MFMAs of tile j+1 are issued while the VALU
-//    runs the softmax of tile j, and the P V MFMAs of tile j while the row sums, the bf16
-//    packing and the LDS stores of tile j+2 run; independent MFMA and VALU work from one wave
-//    overlaps on CDNA;
-//  * V is transposed in registers on its way into LDS, so the V^T operand is one ds_read_b128
-//    per lane; K and V^T tiles use XOR-swizzled 16-byte chunks (8 rows read by 8 neighbouring
-//    lanes fall in distinct banks); three LDS buffers, one barrier per tile, global loads two
-//    tiles ahead;
-//  * K/V/Q/O go through buffer instructions whose resource ends at the last valid row, so
-//    rows past N read as zero and stores past N are dropped, without per-lane branches;
+//  * K/V tiles land in LDS through direct-to-LDS buffer loads (no register staging), three
+//    tiles ahead in a four-buffer ring, one barrier per tile; K is read row-wise and V through
+//    ds_read_b64_tr_b16 (the V^T operand straight from the row-major tile); each tensor's
+//    16-byte chunks are XOR-swizzled by row so both read patterns are free of bank conflicts;
+//  * the next tile's score MFMAs are issued in the same branch-free region as this tile's
+//    exponentials and P V MFMAs, so independent MFMA and VALU work of a wave overlaps, and the
+//    two waves of each SIMD fill each other's gaps;
 //  * scores stay in base-2 units (scale * log2 e folded into one FMA before v_exp_f32); the
-//    rescale of the output accumulator is skipped when no row maximum moved;
-//  * causal: tiles wholly above a wave's rows are skipped, diagonal tiles are masked from global
-//    indices, query blocks are scheduled longest-first inside XCD-contiguous task ranges.
+//    reference max only moves when a row's max grows by more than 2^8, so the O rescale is a
+//    rare, wave-uniform branch;
+//  * Q/O go through buffer instructions whose resource ends at the last valid row, so rows
+//    past N read as zero and stores past N are dropped, without per-lane branches;
+//  * causal: tiles wholly above a wave's rows are skipped and only the last one or two are
+//    masked; tasks run longest first, each XCD keeping its own heads (one L2 per head's K/V);
+//    non-causal tasks take XCD-contiguous ranges for the same reason.
 #include "fa_device.h"
 #include "fa_internal.h"
 
