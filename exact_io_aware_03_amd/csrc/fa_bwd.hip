@@ -49,13 +49,14 @@ __device__ __forceinline__ int t_swz(int row) {
 template <int D>
 struct BwdLds {
   static constexpr int ROW = D * 2;
-  static constexpr int KT = BK * ROW;      // K or V, row-major [key][d]
-  static constexpr int QT = BQ * ROW;      // one Q or dO tile, row-major [q][d]
-  static constexpr int OFF_K = 0;
-  static constexpr int OFF_V = OFF_K + KT;
-  static constexpr int OFF_Q = OFF_V + KT;          // Q[2]
+  static constexpr int KT = BK * ROW;      // K or V block in MFMA fragment order
+  static constexpr int QT = BQ * ROW;      // one Q or dO tile, row-major [q][d], swizzled
+  // Q and dO first: their reads take the buffer offset as an instruction immediate (< 64 KiB)
+  static constexpr int OFF_Q = 0;                   // Q[2]
   static constexpr int OFF_DO = OFF_Q + 2 * QT;     // dO[2]
-  static constexpr int OFF_L = OFF_DO + 2 * QT;     // L[2][BQ] fp32 (natural log)
+  static constexpr int OFF_K = OFF_DO + 2 * QT;
+  static constexpr int OFF_V = OFF_K + KT;
+  static constexpr int OFF_L = OFF_V + KT;          // L[2][BQ] fp32 (natural log)
   static constexpr int OFF_D = OFF_L + 2 * BQ * 4;  // D[2][BQ] fp32
   static constexpr int BYTES = OFF_D + 2 * BQ * 4;
   static constexpr int RR = 1024 / ROW;             // rows per 1 KiB direct-to-LDS load
@@ -133,6 +134,30 @@ __device__ __forceinline__ void dma_rows(char* dst, const uint16_t* src, long ro
   }
 }
 
+// Direct-to-LDS loads of a K or V block in MFMA fragment order: the 1 KiB region
+// R = (D/16)*slice + ks holds at byte 16 l the 8 values that lane l feeds to the score product
+// of 32-key slice `slice` and 16-dim step ks -- key 32 slice + l%32, dims 16 ks + 8(l/32) .. +7
+// -- so those reads are lane-contiguous (no bank conflicts) at constant offsets from one
+// per-lane base. Keys at or past `valid_rows` read as zero.
+template <int D, int NLOAD>
+__device__ __forceinline__ void dma_frag(char* dst, const uint16_t* src, long row_stride, int valid_rows) {
+  constexpr int KS = D / 16;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const u32x4 r = dma_rsrc(src, ((long)(valid_rows - 1) * row_stride + D) * 2);
+#pragma unroll
+  for (int p = 0; p < NLOAD; ++p) {
+    const int region = kWaves * p + w;
+    const int row = 32 * (region / KS) + (lane & 31);
+    const int voff = (int)((row * row_stride + 16 * (region % KS) + 8 * (lane >> 5)) * 2);
+    lds_dma16(r, dst + region * 1024, voff);
+  }
+}
+
+template <int N>
+struct Const {
+  static constexpr int value = N;
+};
+
 // A operand of a transposed product read from a row-major LDS tile with two
 // ds_read_b64_tr_b16: lane l receives column c0 + l%32 (c0 = 32*cb) and the 8 consecutive rows
 // 16ks + 8(l/32) .. +7. In each 16-lane group, source lane s points at row r0 + s/4,
@@ -209,10 +234,9 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(BwdArgs a) {
   const uint16_t* kp = (const uint16_t*)a.k + (long)b * a.Nk * a.k_row + hk * D;
   const uint16_t* vp = (const uint16_t*)a.v + (long)b * a.Nk * a.k_row + hk * D;
 
-  // K and V rows of the block, row-major in LDS: B operands of S = Q K^T and dP = dO V^T
-  // (row reads) and of dQ = dS K (transposed reads)
-  dma_rows<D, L::KDMA>(kl, kp + (long)kv0 * a.k_row, a.k_row, a.Nk - kv0);
-  dma_rows<D, L::KDMA>(vl, vp + (long)kv0 * a.k_row, a.k_row, a.Nk - kv0);
+  // K and V of the block in LDS, in MFMA fragment order: B operands of S = Q K^T and dP = dO V^T
+  dma_frag<D, L::KDMA>(kl, kp + (long)kv0 * a.k_row, a.k_row, a.Nk - kv0);
+  dma_frag<D, L::KDMA>(vl, vp + (long)kv0 * a.k_row, a.k_row, a.Nk - kv0);
 
   f32x16 dk[DB], dv[DB];
 #pragma unroll
@@ -239,65 +263,90 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(BwdArgs a) {
     else lds_dma4(dma_rsrc(a.dvec + loff, lbytes), smem + L::OFF_D + buf * BQ * 4, lane * 4);
   };
 
-  issue_step(0);
-  for (int st = 0; st < n_steps; ++st) {
+  // Per-lane LDS byte offsets, fixed for the whole task; the buffer, tensor and step parts of
+  // every address are compile-time constants that go into the instructions' offset field.
+  // Q / dO as A operands of S and dP: row 32 qhalf + relabelled l32, logical chunk 2 ks + h.
+  int qoff[KS];
+  {
+    const int row = 32 * qhalf + swap_bits23(l32);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qoff[ks] = row * L::ROW + (((2 * ks + h) ^ t_swz<D>(row)) << 4);
+  }
+  // dO / Q as transposed B operands of dV and dK (two ds_read_b64_tr_b16 per fragment): in each
+  // 16-lane group, source lane s points at row r0 + s/4 of the 16-row step, columns
+  // 32 db + 16((l/16)%2) + 4(s%4) .. +3; lane l receives column 32 db + l%32 and 8 consecutive
+  // rows. The swizzle depends on the row's position within the 16-row step only.
+  int troff[DB][2];
+  {
+    const int sl = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int rd = 0; rd < 2; ++rd) {
+        const int rr = 8 * (g >> 1) + 4 * rd + (sl >> 2);
+        const int col_b = (32 * db + 16 * (g & 1) + 4 * (sl & 3)) * 2;
+        troff[db][rd] = (32 * qhalf + rr) * L::ROW + (((col_b >> 4) ^ t_swz<D>(rr)) << 4) + (col_b & 15);
+      }
+  }
+  const int kvb = L::OFF_K + slice * KS * 1024 + lane * 16;  // K fragments; V at +KT
+  const int lb = L::OFF_L + (32 * qhalf + 8 * h) * 4;        // L rows of this lane; D at +2BQ*4
+  auto ld16 = [&](int off) { return *(const bf16x8*)(smem + off); };
+  auto ld4f = [&](int off) { return *(const f32x4*)(smem + off); };
+  auto tr8 = [&](int off0, int off1) {
+    const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(smem + off0));
+    const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(smem + off1));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    return __builtin_bit_cast(bf16x8, (i16x8)__builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  // One step; the loop below is unrolled by two so the double-buffer index is a constant.
+  auto step = [&](const int st, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
+    constexpr int QB = L::OFF_Q + BUF * L::QT, GB = L::OFF_DO + BUF * L::QT;
     const int q0 = (qb_first + st % per_head) * BQ;
     // This step's loads (and, at st = 0, the K/V tiles) have landed, and every wave is done
     // with the previous step, whose buffer the next step's loads refill: issue them only now.
     wait_vm_barrier<0>();
     if (st + 1 < n_steps) issue_step(st + 1);
-    // LDS addresses are recomputed each step from a pinned copy of the lane index instead of
-    // being hoisted out of the loop: VALU time is cheap here, registers are not.
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const int lh = ln >> 5, ll = ln & 31;
-    const int buf = st & 1;
-    const char* ql = smem + L::OFF_Q + buf * L::QT;
-    const char* dol = smem + L::OFF_DO + buf * L::QT;
-    const float* lls = (const float*)(smem + L::OFF_L + buf * BQ * 4);
-    const float* dls = (const float*)(smem + L::OFF_D + buf * BQ * 4);
 
     // ---- S = Q K^T and dP = dO V^T for this wave's 32 rows x 32 keys ----
     // (causal blocks entirely above this wave's keys run too: their P is masked to zero)
     f32x16 s, g;
     zero16(s);
     zero16(g);
-    {
-      const int row = 32 * qhalf + swap_bits23(ll);  // A operand rows (relabelled)
-      const int sw = t_swz<D>(row);
-      const int kr = 32 * slice + ll;                // B operand: this lane's key row
-      const int ksw = t_swz<D>(kr);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int off = row * L::ROW + (((2 * ks + lh) ^ sw) << 4);
-        const int koff = kr * L::ROW + (((2 * ks + lh) ^ ksw) << 4);
-        s = mfma_32x32x16(*(const bf16x8*)(ql + off), *(const bf16x8*)(kl + koff), s);
-        g = mfma_32x32x16(*(const bf16x8*)(dol + off), *(const bf16x8*)(vl + koff), g);
-      }
+    for (int ks = 0; ks < KS; ++ks) {
+      s = mfma_32x32x16(ld16(qoff[ks] + QB), ld16(kvb + ks * 1024), s);
+      g = mfma_32x32x16(ld16(qoff[ks] + GB), ld16(kvb + L::KT + ks * 1024), g);
     }
-    // register i holds query row 32qhalf + (i&7) + 8h + 16(i>>3) and key `key`: the 8 rows
-    // (i&7) are consecutive, so L and D come in as 16-byte LDS reads.
+    // register i holds query row 32qhalf + (i&7) + 8h + 16(i>>3) and key `key`
     const int qw0 = q0 + 32 * qhalf;  // first row of this wave's half
-    const bool need_mask = kw0 + 31 >= a.Nk || (a.causal && kw0 + 31 > qw0);
+    if (kw0 + 31 >= a.Nk || (a.causal && kw0 + 31 > qw0)) {
+      // key past the end: every row masked; causal: rows before the key masked
+      const int first_row = key >= a.Nk ? 0x7fffffff : (a.causal ? key : 0);
+      const int thr = first_row == 0x7fffffff ? 64 : first_row - qw0 - 8 * h;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = (i & 7) + 16 * (i >> 3) < thr ? kNegInf : s[i];
+    }
+    // P = exp(scale S - L), dS = P (dP - D); the 8 rows (i&7) are consecutive, so L and D
+    // come in as 16-byte LDS reads
 #pragma unroll
     for (int hi = 0; hi < 2; ++hi) {
-      const int r0 = 32 * qhalf + 16 * hi + 8 * lh;
-      const f32x4 la = *(const f32x4*)(lls + r0), lb = *(const f32x4*)(lls + r0 + 4);
-      const f32x4 da = *(const f32x4*)(dls + r0), dbv = *(const f32x4*)(dls + r0 + 4);
+      const int lo = lb + BUF * BQ * 4 + 64 * hi;
+      const f32x4 la = ld4f(lo), lbv = ld4f(lo + 16);
+      const f32x4 da = ld4f(lo + 2 * BQ * 4), dbv = ld4f(lo + 2 * BQ * 4 + 16);
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
         const int i = 8 * hi + x;
-        const float lv = x < 4 ? la[x] : lb[x - 4], dvv = x < 4 ? da[x] : dbv[x - 4];
-        float p = fast_exp2(fmaf(s[i], a.c, -lv * kLog2e));
-        if (need_mask && (key >= a.Nk || (a.causal && key > q0 + r0 + x))) p = 0.f;
-        s[i] = p;                   // P
+        const float lv = x < 4 ? la[x] : lbv[x - 4], dvv = x < 4 ? da[x] : dbv[x - 4];
+        const float p = fast_exp2(fmaf(s[i], a.c, -lv * kLog2e));
+        s[i] = p;                  // P
         g[i] = p * (g[i] - dvv);  // dS
       }
     }
-    // ---- dV += P^T dO, dK += dS^T Q over this wave's 32 rows (16 per step) ----
+    // ---- dV += P^T dO, dK += dS^T Q over this wave's 32 rows (16 per product) ----
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const int kq = 2 * qhalf + kk;  // 16-row step within the 64-row block
       const int e = kk * 8;
       u32x4 pw, gw;
 #pragma unroll
@@ -305,13 +354,22 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(BwdArgs a) {
         pw[x] = pack_bf16x2(s[e + 2 * x], s[e + 2 * x + 1]);
         gw[x] = pack_bf16x2(g[e + 2 * x], g[e + 2 * x + 1]);
       }
+      constexpr int R16 = 16 * L::ROW;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        dv[db] = mfma_32x32x16(as_bf16x8(pw), tr_frag<L::ROW>(dol, kq, db, ln, t_swz<D>), dv[db]);
-        dk[db] = mfma_32x32x16(as_bf16x8(gw), tr_frag<L::ROW>(ql, kq, db, ln, t_swz<D>), dk[db]);
+        dv[db] = mfma_32x32x16(as_bf16x8(pw), tr8(troff[db][0] + GB + kk * R16, troff[db][1] + GB + kk * R16), dv[db]);
+        dk[db] = mfma_32x32x16(as_bf16x8(gw), tr8(troff[db][0] + QB + kk * R16, troff[db][1] + QB + kk * R16), dk[db]);
       }
     }
+  };
+
+  issue_step(0);
+  int st = 0;
+  for (; st + 1 < n_steps; st += 2) {
+    step(st, Const<0>{});
+    step(st + 1, Const<1>{});
   }
+  if (st < n_steps) step(st, Const<0>{});
   __builtin_amdgcn_s_waitcnt(0);
 
   // ---- reduce the two query halves' partials; dK = scale * acc, dV = acc (bf16) ----
@@ -441,17 +499,45 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   dq_dma_tile<D>(smem + T::BUF, kp, vp, a.k_row, DQ_BC, nk_load);
   dq_dma_tile<D>(smem + 2 * T::BUF, kp, vp, a.k_row, 2 * DQ_BC, nk_load);
 
-  for (int j = 0; j < n_tiles; ++j) {
+  // Per-lane LDS byte offsets within a tile buffer, fixed for the whole task; the buffer,
+  // tensor and step parts of each address are constants in the instructions' offset field.
+  // K / V rows as A operands of S^T and dP^T: row 32 kb + relabelled l32, logical chunk 2 ks + h.
+  int roff[2][KS];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int row = 32 * kb + swap_bits23(l32);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) roff[kb][ks] = row * T::ROW + (((2 * ks + h) ^ t_swz<D>(row)) << 4);
+  }
+  // K^T as the A operand of dQ^T (two ds_read_b64_tr_b16 per fragment, as in the dK/dV kernel)
+  int troff[DB][2];
+  {
+    const int sl = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int rd = 0; rd < 2; ++rd) {
+        const int rr = 8 * (g >> 1) + 4 * rd + (sl >> 2);
+        const int col_b = (32 * db + 16 * (g & 1) + 4 * (sl & 3)) * 2;
+        troff[db][rd] = rr * T::ROW + (((col_b >> 4) ^ t_swz<D>(rr)) << 4) + (col_b & 15);
+      }
+  }
+  auto ld16 = [&](int off) { return *(const bf16x8*)(smem + off); };
+  auto tr8 = [&](int off0, int off1) {
+    const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(smem + off0));
+    const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(smem + off1));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    return __builtin_bit_cast(bf16x8, (i16x8)__builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  // One tile; the buffer index j % DQ_NBUF is a compile-time constant in each copy.
+  auto tile = [&](const int j, auto bufc) {
+    constexpr int KB = decltype(bufc)::value * T::BUF, VB = KB + T::T_BYTES;
     // tile j landed (tiles j+1 and j+2 may be pending); every wave is done with tile j-1,
     // whose buffer the prefetch of tile j+3 refills
     wait_vm_barrier<2 * T::VMCNT>();
     dq_dma_tile<D>(smem + ((j + 3) % DQ_NBUF) * T::BUF, kp, vp, a.k_row, (j + 3) * DQ_BC, nk_load);
-    if (j > last_w) continue;
-    const char* kt = smem + (j % DQ_NBUF) * T::BUF;
-    const char* vt = kt + T::T_BYTES;
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const int lh = ln >> 5, ll = ln & 31;
+    if (j > last_w) return;
     const int kv0 = j * DQ_BC;
 
     // ---- S^T and dP^T for 64 keys (two 32-key blocks) x this wave's 32 queries ----
@@ -460,27 +546,27 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dq_kernel(BwdArgs a) {
     for (int kb = 0; kb < 2; ++kb) {
       zero16(s[kb]);
       zero16(g[kb]);
-      const int row = 32 * kb + swap_bits23(ll);
-      const int sw = t_swz<D>(row);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int off = row * T::ROW + (((2 * ks + lh) ^ sw) << 4);
-        s[kb] = mfma_32x32x16(*(const bf16x8*)(kt + off), qf[ks], s[kb]);
-        g[kb] = mfma_32x32x16(*(const bf16x8*)(vt + off), gf[ks], g[kb]);
+        s[kb] = mfma_32x32x16(ld16(roff[kb][ks] + KB), qf[ks], s[kb]);
+        g[kb] = mfma_32x32x16(ld16(roff[kb][ks] + VB), gf[ks], g[kb]);
       }
       fence();  // bounds the K/V fragments in flight (register budget)
     }
     // register i of block kb holds key kv0 + 32kb + (i&7) + 8h + 16(i>>3), query qi
-    const bool need_mask = kv0 + DQ_BC > a.Nk || (CAUSAL && kv0 + DQ_BC - 1 > q0);
+    if (kv0 + DQ_BC > a.Nk || (CAUSAL && kv0 + DQ_BC - 1 > q0)) {
+      // keys at or past min(Nk, qi + 1 when causal) are masked
+      const int thr = (CAUSAL ? min(a.Nk, qi + 1) : a.Nk) - kv0 - 8 * h;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb][i] = 32 * kb + (i & 7) + 16 * (i >> 3) >= thr ? kNegInf : s[kb][i];
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float p = fast_exp2(fmaf(s[kb][i], a.c, -l2));
-        if (need_mask) {
-          const int key = kv0 + 32 * kb + (i & 7) + 8 * h + 16 * (i >> 3);
-          if (key >= a.Nk || (CAUSAL && key > qi)) p = 0.f;
-        }
+        const float p = fast_exp2(fmaf(s[kb][i], a.c, -l2));
         g[kb][i] = p * (g[kb][i] - dd);  // dS
       }
     // ---- dQ^T += K^T dS^T: 16-key step kk takes dS registers 8(kk&1) .. +7 of block kk/2 ----
@@ -491,10 +577,21 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dq_kernel(BwdArgs a) {
       u32x4 gw;
 #pragma unroll
       for (int x = 0; x < 4; ++x) gw[x] = pack_bf16x2(gs[e + 2 * x], gs[e + 2 * x + 1]);
+      constexpr int R16 = 16 * T::ROW;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        acc[db] = mfma_32x32x16(tr_frag<T::ROW>(kt, kk, db, ln, t_swz<D>), as_bf16x8(gw), acc[db]);
+        acc[db] = mfma_32x32x16(tr8(troff[db][0] + KB + kk * R16, troff[db][1] + KB + kk * R16), as_bf16x8(gw),
+                                acc[db]);
     }
+  };
+  // unrolled by the ring size; the iteration count is padded to a multiple of it (the extra
+  // iterations only keep the barrier count and prefetch nothing)
+  static_assert(DQ_NBUF == 4, "one tile copy per buffer");
+  for (int j = 0; j < n_tiles; j += 4) {
+    tile(j, Const<0>{});
+    tile(j + 1, Const<1>{});
+    tile(j + 2, Const<2>{});
+    tile(j + 3, Const<3>{});
   }
   __builtin_amdgcn_s_waitcnt(0);  // drain the tail prefetches before the workgroup ends
 

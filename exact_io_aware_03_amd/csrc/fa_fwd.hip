@@ -169,17 +169,15 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[QH][2], int kv0, int nk, i
 }
 
 __device__ __forceinline__ float max32(const f32x16& a, const f32x16& b) {
-  float m0 = fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
-  float m1 = fmaxf(fmaxf(a[4], a[5]), fmaxf(a[6], a[7]));
-  float m2 = fmaxf(fmaxf(a[8], a[9]), fmaxf(a[10], a[11]));
-  float m3 = fmaxf(fmaxf(a[12], a[13]), fmaxf(a[14], a[15]));
-  float m4 = fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3]));
-  float m5 = fmaxf(fmaxf(b[4], b[5]), fmaxf(b[6], b[7]));
-  float m6 = fmaxf(fmaxf(b[8], b[9]), fmaxf(b[10], b[11]));
-  float m7 = fmaxf(fmaxf(b[12], b[13]), fmaxf(b[14], b[15]));
-  return fmaxf(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)), fmaxf(fmaxf(m4, m5), fmaxf(m6, m7)));
+  // two chains of three-input maxima (v_max3_f32), one per accumulator
+  float x = fmaxf(fmaxf(a[0], a[1]), a[2]), y = fmaxf(fmaxf(b[0], b[1]), b[2]);
+#pragma unroll
+  for (int i = 3; i < 15; i += 2) {
+    x = fmaxf(fmaxf(x, a[i]), a[i + 1]);
+    y = fmaxf(fmaxf(y, b[i]), b[i + 1]);
+  }
+  return fmaxf(fmaxf(x, a[15]), fmaxf(y, b[15]));
 }
-
 __device__ __forceinline__ float sum32(const f32x16& a, const f32x16& b) {
   float s0 = (a[0] + a[1]) + (a[2] + a[3]), s1 = (a[4] + a[5]) + (a[6] + a[7]);
   float s2 = (a[8] + a[9]) + (a[10] + a[11]), s3 = (a[12] + a[13]) + (a[14] + a[15]);
@@ -216,7 +214,8 @@ template <int D, bool CAUSAL, bool NEXT>
 __device__ __forceinline__ void tile_step(char* smem, int j, const uint16_t* kp, const uint16_t* vp, long k_row,
                                           int nk_load, int nk, const TileDma<D>& dm, int q0, int l32, int h, int lane,
                                           int krow0, float c, const bf16x8 (&qf)[QH][D / 16], f32x16 (&s)[QH][2],
-                                          f32x16 (&o)[QH][D / 32], float (&m)[QH], float (&l)[QH]) {
+                                          f32x16 (&sn)[QH][2], f32x16 (&o)[QH][D / 32], float (&m)[QH],
+                                          float (&l)[QH]) {
   using T = Tile<D>;
   const int kv0 = j * BC;
   const char* cur = smem + (j % NBUF) * T::BUF;
@@ -251,7 +250,6 @@ __device__ __forceinline__ void tile_step(char* smem, int j, const uint16_t* kp,
   }
 
   // ---- phase A: scores of tile j+1 (MFMA) interleaved with the softmax of tile j (VALU) ----
-  f32x16 sn[QH][2];
   if (NEXT) scores<D>(smem + ((j + 1) % NBUF) * T::BUF, krow0, h, qf, sn);
 #pragma unroll
   for (int qh = 0; qh < QH; ++qh)
@@ -285,12 +283,6 @@ __device__ __forceinline__ void tile_step(char* smem, int j, const uint16_t* kp,
   for (int qh = 0; qh < QH; ++qh) l[qh] = l[qh] * alpha[qh] + sum32(s[qh][0], s[qh][1]);
 
   wait_vm_barrier<T::VMCNT>();  // tile j+2 landed; tile j+3 may still be in flight
-  if (NEXT) {
-#pragma unroll
-    for (int qh = 0; qh < QH; ++qh)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s[qh][kb] = sn[qh][kb];
-  }
 }
 
 template <int D, bool CAUSAL>
@@ -365,15 +357,28 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   wait_vm_barrier<T::VMCNT>();
 
   const int krow0 = swap_bits23(l32);
-  f32x16 s[QH][2];
-  scores<D>(smem, krow0, h, qf, s);
+  // scores alternate between two register sets (the loop is unrolled by two tiles), so the
+  // next tile's scores never need copying
+  f32x16 s0[QH][2], s1[QH][2];
+  scores<D>(smem, krow0, h, qf, s0);
 
   int j = 0;
-  for (; j < last_w; ++j)
-    tile_step<D, CAUSAL, true>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, a.c, qf, s, o, m,
-                               l);
-  tile_step<D, CAUSAL, false>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, a.c, qf, s, o, m,
-                              l);
+  for (; j + 1 < last_w; j += 2) {
+    tile_step<D, CAUSAL, true>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, a.c, qf, s0, s1,
+                               o, m, l);
+    tile_step<D, CAUSAL, true>(smem, j + 1, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, a.c, qf, s1,
+                               s0, o, m, l);
+  }
+  if (j < last_w) {
+    tile_step<D, CAUSAL, true>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, a.c, qf, s0, s1,
+                               o, m, l);
+    ++j;
+    tile_step<D, CAUSAL, false>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, a.c, qf, s1,
+                                s0, o, m, l);
+  } else {
+    tile_step<D, CAUSAL, false>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, a.c, qf, s0,
+                                s1, o, m, l);
+  }
   ++j;
   // tiles past this wave's diagonal: keep the workgroup's barrier count
   for (; j < n_tiles; ++j) {
