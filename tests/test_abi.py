@@ -51,6 +51,8 @@ def fwd(**kw):
         (dict(scale=float("inf")), INVALID),
         (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(dtype=7), UNSUPPORTED),
         (dict(causal=1, Nq=8, Nk=9), UNSUPPORTED),
+        # one batch of Q/O or K/V must stay below 2 GiB (32-bit buffer offsets)
+        (dict(Nq=1 << 20, Hq=8, Hkv=8, d=128), UNSUPPORTED), (dict(Nk=1 << 23, Hq=1, Hkv=1, d=128), UNSUPPORTED),
     ],
 )
 def test_fwd_validation(kw, code):
@@ -76,6 +78,8 @@ def test_bwd_validation():
     assert bwd(Hq=2, Hkv=3) == INVALID
     assert bwd(causal=1, Nk=9) == UNSUPPORTED
     assert bwd(d=32) == UNSUPPORTED
+    assert bwd(Nq=1 << 20, Nk=8, Hq=8, Hkv=8, d=128) == UNSUPPORTED  # 2 GiB per batch of Q
+    assert bwd(Nk=1 << 23, Hq=1, Hkv=1, d=128) == UNSUPPORTED  # 2 GiB per batch of K
     assert fa.lib().fa_bwd(None, P, P, P, P, P, P, P, P, 1, 2, 1, 8, 8, 64, 0, 0.1, 1, P, need, None) == INVALID
 
 

@@ -71,19 +71,23 @@ def run_fwd_bwd(inp, causal, scale):
 
 
 @pytest.mark.parametrize(
-    "B,N,Hq,Hkv,d,causal",
+    "B,Nq,Nk,Hq,Hkv,d,causal",
     [
-        (1, 128, 1, 1, 128, False),
-        (1, 128, 1, 1, 128, True),
-        (2, 300, 2, 2, 128, True),   # ragged
-        (1, 200, 4, 2, 64, False),   # GQA, d = 64
-        (1, 257, 4, 1, 128, True),   # GQA 4:1, ragged
-        (1, 64, 2, 2, 64, True),
+        (1, 128, 128, 1, 1, 128, False),
+        (1, 128, 128, 1, 1, 128, True),
+        (2, 300, 300, 2, 2, 128, True),   # ragged
+        (1, 200, 200, 4, 2, 64, False),   # GQA, d = 64
+        (1, 257, 257, 4, 1, 128, True),   # GQA 4:1, ragged
+        (1, 64, 64, 2, 2, 64, True),
+        (1, 100, 333, 2, 1, 128, False),  # N_q != N_k, both ragged
+        (1, 520, 70, 2, 1, 64, False),    # more query rows than keys
+        (1, 1, 1, 1, 1, 128, False),      # one query, one key: dS = 0, dV = dO
     ],
 )
-def test_bwd_small(B, N, Hq, Hkv, d, causal):
-    say(f"bwd B={B} N={N} Hq={Hq} Hkv={Hkv} d={d} causal={causal}")
-    inp = workloads.make_attention_inputs(B, N, N, Hq, Hkv, d, seed=900 + N + d, with_do=True)
+def test_bwd_small(B, Nq, Nk, Hq, Hkv, d, causal):
+    say(f"bwd B={B} Nq={Nq} Nk={Nk} Hq={Hq} Hkv={Hkv} d={d} causal={causal}")
+    seed = 900 + Nq + d if Nq == Nk else 950 + Nq + 3 * Nk + d
+    inp = workloads.make_attention_inputs(B, Nq, Nk, Hq, Hkv, d, seed=seed, with_do=True)
     scale = 1.0 / math.sqrt(d)
     dq, dk, dv = run_fwd_bwd(inp, causal, scale)
     rq, rk, rv = ora.backward(inp["q"], inp["k"], inp["v"], inp["do"], causal, scale)
@@ -105,3 +109,37 @@ def test_bwd_config():
         check(f"dQ[b={b},h={g}]", dq[b, :, g], rq[b, :, g], "bf16")
         check(f"dK[b={b},h={g}]", dk[b, :, g], rk[b, :, g], "bf16")
         check(f"dV[b={b},h={g}]", dv[b, :, g], rv[b, :, g], "bf16")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_training_shape(causal):
+    # the shape and launch configuration the benchmark step times, on sampled heads
+    w = workloads.WORKLOADS["fwd_bf16_b16h16n2048d128"]
+    say(f"bwd training shape {w.name} causal={causal}")
+    inp = workloads.make_attention_inputs(w.B, w.Nq, w.Nk, w.Hq, w.Hkv, w.d, seed=w.seed, with_do=True)
+    dq, dk, dv = run_fwd_bwd(inp, causal, w.scale)
+    pairs = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
+    sel = [pairs[i] for i in workloads.sample_indices(len(pairs), 3, 61 + causal)]
+    say(f"  oracle gradients on heads {sel}")
+    rq, rk, rv = ora.backward(inp["q"], inp["k"], inp["v"], inp["do"], causal, w.scale, heads=sel)
+    for b, g in sel:
+        check(f"dQ[b={b},h={g}]", dq[b, :, g], rq[b, :, g], "bf16")
+        check(f"dK[b={b},h={g}]", dk[b, :, g], rk[b, :, g], "bf16")
+        check(f"dV[b={b},h={g}]", dv[b, :, g], rv[b, :, g], "bf16")
+
+
+def test_bwd_and_fwd_are_reproducible():
+    # no atomics and a fixed summation order: two calls give bit-identical results
+    import torch
+
+    fa = _fa()
+    inp = workloads.make_attention_inputs(2, 700, 700, 4, 2, 128, seed=4242, with_do=True)
+    q, k, v, do = (to_dev(inp[n], "bf16") for n in ("q", "k", "v", "do"))
+    runs = []
+    for _ in range(2):
+        o, lse = fa.forward(q, k, v, causal=True, scale=0.1)
+        dq, dk, dv = fa.backward(q, k, v, o, do, lse, causal=True, scale=0.1)
+        torch.cuda.synchronize()
+        runs.append([t.clone() for t in (o, lse, dq, dk, dv)])
+    for a, b in zip(*runs):
+        assert torch.equal(a, b)
