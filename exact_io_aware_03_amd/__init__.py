@@ -23,7 +23,7 @@ _STATUS = {0: "FA_OK", -1: "FA_ERR_INVALID_ARG", -2: "FA_ERR_UNSUPPORTED", -3: "
 EXPORTED = (
     "fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_workspace_size", "fa_strerror",
     "fa_version", "fa_wave_efficiency", "fa_plan_splits", "fa_schedule_makespan", "fa_causal_tiles",
-    "fa_decode_chunk",
+    "fa_decode_chunk", "fa_fp8_scale_count", "fa_quantize_fp8", "fa_fwd_fp8",
 )
 
 _lib = None
@@ -67,6 +67,12 @@ def lib() -> ctypes.CDLL:
     L.fa_causal_tiles.restype = ctypes.c_long
     L.fa_decode_chunk.argtypes = [i, i, i]
     L.fa_decode_chunk.restype = i
+    L.fa_fp8_scale_count.argtypes = [i, i, i]
+    L.fa_fp8_scale_count.restype = sz
+    L.fa_quantize_fp8.argtypes = [vp] * 4 + [i] * 4 + [vp]
+    L.fa_quantize_fp8.restype = i
+    L.fa_fwd_fp8.argtypes = [vp] * 7 + [i] * 7 + [f, vp]
+    L.fa_fwd_fp8.restype = i
     _lib = L
     return L
 
@@ -138,6 +144,25 @@ def fa_decode(q, k_cache, v_cache, seqlens, o, lse, workspace, scale: float | No
                            Nq, Nk_max, d, scale, _dtype_code(q), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
+def fa_quantize_fp8(x, signs, x8, scales, stream=None) -> None:
+    """E4M3 codes and per-64-row block scales of a bf16 [B,N,H,d] tensor, rotated by
+    diag(signs) H_d / sqrt(d) first when `signs` (d fp32 values of +-1) is given."""
+    _need_contig(x, signs, x8, scales)
+    B, N, H, d = x.shape
+    _check(lib().fa_quantize_fp8(_ptr(x), _ptr(signs), _ptr(x8), _ptr(scales), B, N, H, d, _stream(stream)))
+
+
+def fa_fwd_fp8(q8, k8, v, q_scale, k_scale, o, lse, causal: bool = False, scale: float | None = None,
+               stream=None) -> None:
+    """O and lse from E4M3 q8/k8 (with their block scales) and bf16 v (see include/fa.h)."""
+    _need_contig(q8, k8, v, q_scale, k_scale, o, lse)
+    B, Nq, Hq, d = q8.shape
+    Nk, Hkv = k8.shape[1], k8.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    _check(lib().fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v), _ptr(q_scale), _ptr(k_scale), _ptr(o), _ptr(lse), B, Hq,
+                            Hkv, Nq, Nk, d, int(causal), scale, _stream(stream)))
+
+
 def fa_bwd_workspace_size(B: int, Hq: int, Nq: int, d: int) -> int:
     return int(lib().fa_bwd_workspace_size(B, Hq, Nq, d))
 
@@ -176,6 +201,27 @@ def decode(q, k_cache, v_cache, seqlens, scale: float | None = None, stream=None
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     fa_decode(q, k_cache, v_cache, seqlens, o, lse, ws, scale, stream)
+    return o, lse
+
+
+def quantize_fp8(x, signs=None, stream=None):
+    """(codes uint8 [B,N,H,d], scales fp32 [B,H,ceil(N/64)]) of a bf16 tensor."""
+    import torch
+
+    B, N, H, _ = x.shape
+    x8 = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    scales = torch.empty((B, H, (N + 63) // 64), dtype=torch.float32, device=x.device)
+    fa_quantize_fp8(x, signs, x8, scales, stream)
+    return x8, scales
+
+
+def forward_fp8(q8, k8, v, q_scale, k_scale, causal: bool = False, scale: float | None = None, stream=None):
+    import torch
+
+    B, Nq, Hq, d = q8.shape
+    o = torch.empty((B, Nq, Hq, d), dtype=torch.bfloat16, device=q8.device)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q8.device)
+    fa_fwd_fp8(q8, k8, v, q_scale, k_scale, o, lse, causal, scale, stream)
     return o, lse
 
 

@@ -31,7 +31,7 @@ COMMON = [
     # keep the compiler from forming v_pk_{add,mul,fma}_f32 (host pass warns it does not know it)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_decode.hip", "fa_bwd.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fp8.hip", "fa_decode.hip", "fa_bwd.hip"]
 
 
 def _compile(src: str, opt: list[str]) -> str:

@@ -80,6 +80,50 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   return hip_status(dtype == FA_BF16 ? fa::launch_fwd_bf16(a, d, s) : fa::launch_fwd_f32(a, d, s));
 }
 
+size_t fa_fp8_scale_count(int B, int N, int H) {
+  if (B < 1 || N < 1 || H < 1) return 0;
+  return (size_t)B * H * ((N + fa::kFp8Block - 1) / fa::kFp8Block);
+}
+
+int fa_quantize_fp8(const void* x, const float* signs, void* x8, float* scales, int B, int N, int H, int d,
+                    void* stream) {
+  if (!x || !x8 || !scales) return FA_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(x8) || !aligned16(scales) || (signs && !aligned16(signs))) return FA_ERR_INVALID_ARG;
+  if (B < 1 || N < 1 || H < 1) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if ((long)B * H * ((N + fa::kFp8Block - 1) / fa::kFp8Block) > INT_MAX) return FA_ERR_INVALID_ARG;
+  return hip_status(fa::launch_quantize_fp8(x, signs, x8, scales, B, N, H, d, (hipStream_t)stream));
+}
+
+int fa_fwd_fp8(const void* q8, const void* k8, const void* v, const float* q_scale, const float* k_scale, void* o,
+               float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale, void* stream) {
+  if (!q8 || !k8 || !v || !q_scale || !k_scale || !o || !lse) return FA_ERR_INVALID_ARG;
+  for (const void* p : {q8, k8, v, (const void*)q_scale, (const void*)k_scale, (const void*)o, (const void*)lse})
+    if (!aligned16(p)) return FA_ERR_INVALID_ARG;
+  int st = common_checks(B, Hq, Hkv, Nq, Nk, d, scale);
+  if (st != FA_OK) return st;
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  if (causal && Nq != Nk) return FA_ERR_UNSUPPORTED;
+  // buffer-resource offsets are 32-bit: one batch of O (bf16) or V (bf16) must stay below 2 GiB
+  if ((long)Nq * Hq * d * 2 >= (1L << 31) || (long)Nk * Hkv * d * 2 >= (1L << 31)) return FA_ERR_UNSUPPORTED;
+  fa::FwdArgs a{};
+  a.q = q8; a.k = k8; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.G = Hq / Hkv;
+  a.q_row = (long)Hq * d;
+  a.k_row = (long)Hkv * d;
+  a.c = scale * 1.4426950408889634f;
+  a.causal = causal ? 1 : 0;
+  a.n_qblk = (Nq + fa::kFwdRows - 1) / fa::kFwdRows;
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  a.q_nblk = (Nq + fa::kFp8Block - 1) / fa::kFp8Block;
+  a.k_nblk = (Nk + fa::kFp8Block - 1) / fa::kFp8Block;
+  const long tasks = (long)B * Hq * a.n_qblk;
+  if (tasks > INT_MAX) return FA_ERR_INVALID_ARG;
+  a.n_tasks = (int)tasks;
+  return hip_status(fa::launch_fwd_fp8(a, d, (hipStream_t)stream));
+}
+
 size_t fa_bwd_workspace_size(int B, int Hq, int Nq, int d) {
   if (B < 1 || Hq < 1 || Nq < 1 || d < 1) return 0;
   return align256((size_t)B * Hq * Nq * sizeof(float));  // D = rowsum(dO * O)

@@ -50,15 +50,32 @@ typedef __attribute__((address_space(3))) void lds_t;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
+// Q fragments a wave keeps in registers: bf16 (8 dims per lane per 16-dim step) or E4M3
+// (32 dims per lane per 64-dim step).
+template <int D, bool F8>
+struct QFrag {
+  typedef bf16x8 type[QH][D / 16];
+};
 template <int D>
+struct QFrag<D, true> {
+  typedef i32x8 type[QH][D / 64];
+};
+
+// One K/V tile in LDS: K row-major [key][d] in bf16, or in E4M3 (one byte per value) for the
+// FP8 path, then V row-major in bf16.
+template <int D, bool F8 = false>
 struct Tile {
-  static constexpr int KCH = D / 8;                 // 16-byte chunks per row
-  static constexpr int ROW = D * 2;                 // bytes per K or V row
-  static constexpr int K_BYTES = BC * ROW;          // K tile, row-major [key][d]
-  static constexpr int BUF = 2 * K_BYTES;           // K tile then V tile (both row-major)
-  static constexpr int RR = 1024 / ROW;             // rows one wave-wide 16-byte DMA covers
-  static constexpr int DMA = K_BYTES / 1024 / kWaves;  // DMA instructions per wave per tensor per tile
-  static constexpr int VMCNT = 2 * DMA;             // DMA instructions per thread per tile
+  static constexpr int KE = F8 ? 1 : 2;              // bytes per K value
+  static constexpr int KROW = D * KE;                // bytes per K row
+  static constexpr int ROW = D * 2;                  // bytes per V row
+  static constexpr int KCH = KROW / 16, VCH = ROW / 16;  // 16-byte chunks per row
+  static constexpr int K_BYTES = BC * KROW;
+  static constexpr int BUF = K_BYTES + BC * ROW;     // K tile then V tile
+  static constexpr int KRR = 1024 / KROW, VRR = 1024 / ROW;  // rows one wave-wide 16-byte DMA covers
+  static constexpr int KDMA = K_BYTES / 1024 / kWaves;  // DMA instructions per wave per tile (K)
+  static constexpr int VDMA = BC * ROW / 1024 / kWaves;  // (V)
+  static constexpr int VMCNT = KDMA + VDMA;          // DMA instructions per thread per tile
+  static_assert(KDMA >= 1 && VDMA >= 1, "every wave loads part of each tensor");
 };
 
 // Chunk swizzle of the V tile, read through ds_read_b64_tr_b16 (16 lanes take a 4-row x
@@ -78,23 +95,31 @@ template <int D>
 __device__ __forceinline__ int k_swz(int row) {
   return D == 128 ? (row & 15) : ((row >> 1) & 7);
 }
+// The same for an E4M3 K tile at d=128 (128-byte rows, two per bank line): bits 1-3.
+__device__ __forceinline__ int k8_swz(int row) { return (row >> 1) & 7; }
 
 // Per-lane global byte offsets of the direct-to-LDS loads of one tile: the instruction p of
 // wave w fills 1 KiB of LDS (region kWaves*p+w), lane i landing on row RR*region + i/KCH,
 // physical chunk i%KCH; it fetches the logical chunk that the swizzle puts there.
-template <int D>
+template <int D, bool F8 = false>
 struct TileDma {
-  int k_off[Tile<D>::DMA];
-  int v_off[Tile<D>::DMA];
+  int k_off[Tile<D, F8>::KDMA];
+  int v_off[Tile<D, F8>::VDMA];
   __device__ void init(long k_row) {
-    using T = Tile<D>;
+    using T = Tile<D, F8>;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-    for (int p = 0; p < T::DMA; ++p) {
-      const int row = T::RR * (kWaves * p + w) + lane / T::KCH;
+    for (int p = 0; p < T::KDMA; ++p) {
+      const int row = T::KRR * (kWaves * p + w) + lane / T::KCH;
       const int pc = lane % T::KCH;
-      k_off[p] = (int)((row * k_row + (pc ^ k_swz<D>(row)) * 8) * 2);
-      v_off[p] = (int)((row * k_row + (pc ^ v_swz<D>(row)) * 8) * 2);
+      const int sw = F8 ? k8_swz(row) : k_swz<D>(row);
+      k_off[p] = (int)(row * k_row * T::KE + (pc ^ sw) * 16);
+    }
+#pragma unroll
+    for (int p = 0; p < T::VDMA; ++p) {
+      const int row = T::VRR * (kWaves * p + w) + lane / T::VCH;
+      const int pc = lane % T::VCH;
+      v_off[p] = (int)(row * k_row * 2 + (pc ^ v_swz<D>(row)) * 16);
     }
   }
 };
@@ -107,19 +132,19 @@ __device__ __forceinline__ void lds_dma16(rsrc_t r, char* dst, int voff) {
 
 // Issue the direct-to-LDS loads of the tile starting at key kv0 into `buf`; keys at or past
 // nk land as zero. Completion is tracked by vmcnt (Tile::VMCNT instructions per thread).
-template <int D>
-__device__ __forceinline__ void dma_tile(char* buf, const uint16_t* kp, const uint16_t* vp, long k_row, int kv0,
-                                         int nk, const TileDma<D>& dm) {
-  using T = Tile<D>;
-  const long valid = ((long)(nk - 1 - kv0) * k_row + D) * 2;  // bytes up to the end of the last row
-  const rsrc_t rk = make_rsrc(kp + (long)kv0 * k_row, valid);
-  const rsrc_t rv = make_rsrc(vp + (long)kv0 * k_row, valid);
+// kp / vp: byte addresses of key 0 of this (batch, kv head); k_row: values between keys.
+template <int D, bool F8>
+__device__ __forceinline__ void dma_tile(char* buf, const char* kp, const char* vp, long k_row, int kv0, int nk,
+                                         const TileDma<D, F8>& dm) {
+  using T = Tile<D, F8>;
+  const long valid = (long)(nk - 1 - kv0) * k_row + D;  // values up to the end of the last row
+  const rsrc_t rk = make_rsrc(kp + (long)kv0 * k_row * T::KE, valid * T::KE);
+  const rsrc_t rv = make_rsrc(vp + (long)kv0 * k_row * 2, valid * 2);
   const int w = threadIdx.x >> 6;
 #pragma unroll
-  for (int p = 0; p < T::DMA; ++p) {
-    const int region = (kWaves * p + w) * 1024;
-    lds_dma16(rk, buf + region, dm.k_off[p]);
-    lds_dma16(rv, buf + T::K_BYTES + region, dm.v_off[p]);
+  for (int p = 0; p < T::VDMA; ++p) {
+    if (p < T::KDMA) lds_dma16(rk, buf + (kWaves * p + w) * 1024, dm.k_off[p]);
+    lds_dma16(rv, buf + T::K_BYTES + (kWaves * p + w) * 1024, dm.v_off[p]);
   }
 }
 
@@ -150,6 +175,35 @@ __device__ __forceinline__ void scores(const char* kt, int krow0, int h, const b
       const bf16x8 kf = *(const bf16x8*)(kr + (((2 * ks + h) ^ sw) << 4));
 #pragma unroll
       for (int qh = 0; qh < QH; ++qh) s[qh][kb] = mfma_32x32x16(kf, qf[qh][ks], s[qh][kb]);
+    }
+  }
+}
+
+// The same from an E4M3 K tile and E4M3 Q fragments with v_mfma_f32_32x32x64_f8f6f4 (unit
+// block scales): lane l supplies 32 consecutive dims [64 ks + 32 h, +32) of its K row and of its
+// query, and the accumulator layout is that of the bf16 product, so everything downstream is
+// shared. The raw scores are products of the codes; the block scales multiply them later.
+__device__ __forceinline__ f32x16 mfma_32x32x64_f8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+template <int D>
+__device__ __forceinline__ void scores_f8(const char* kt, int krow0, int h, const i32x8 (&qf)[QH][D / 64],
+                                          f32x16 (&s)[QH][2]) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int row = 32 * kb + krow0;
+    const char* kr = kt + row * D;
+    const int sw = k8_swz(row);
+#pragma unroll
+    for (int qh = 0; qh < QH; ++qh) zero16(s[qh][kb]);
+#pragma unroll
+    for (int ks = 0; ks < D / 64; ++ks) {
+      const int c0 = 4 * ks + 2 * h;
+      const u32x4 lo = *(const u32x4*)(kr + ((c0 ^ sw) << 4));
+      const u32x4 hi = *(const u32x4*)(kr + (((c0 + 1) ^ sw) << 4));
+      const i32x8 kf = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int qh = 0; qh < QH; ++qh) s[qh][kb] = mfma_32x32x64_f8(kf, qf[qh][ks], s[qh][kb]);
     }
   }
 }
@@ -210,17 +264,21 @@ __device__ __forceinline__ bf16x8 v_frag(const char* vt, int ks, int db, int lan
 
 // One K/V tile of the pipelined loop for this wave's rows. On entry s holds the raw scores
 // of tile j; with NEXT, the scores of tile j+1 are produced into s on exit.
-template <int D, bool CAUSAL, bool NEXT>
-__device__ __forceinline__ void tile_step(char* smem, int j, const uint16_t* kp, const uint16_t* vp, long k_row,
-                                          int nk_load, int nk, const TileDma<D>& dm, int q0, int l32, int h, int lane,
-                                          int krow0, float c, const bf16x8 (&qf)[QH][D / 16], f32x16 (&s)[QH][2],
+// c: scale * log2(e) (times this wave's Q block scale on the FP8 path); kscale: the FP8 path's
+// per-tile K block scales.
+template <int D, bool CAUSAL, bool NEXT, bool F8>
+__device__ __forceinline__ void tile_step(char* smem, int j, const char* kp, const char* vp, long k_row, int nk_load,
+                                          int nk, const TileDma<D, F8>& dm, int q0, int l32, int h, int lane,
+                                          int krow0, float c_in, const float* kscale,
+                                          const typename QFrag<D, F8>::type& qf, f32x16 (&s)[QH][2],
                                           f32x16 (&sn)[QH][2], f32x16 (&o)[QH][D / 32], float (&m)[QH],
                                           float (&l)[QH]) {
-  using T = Tile<D>;
+  using T = Tile<D, F8>;
+  const float c = F8 ? c_in * kscale[j] : c_in;
   const int kv0 = j * BC;
   const char* cur = smem + (j % NBUF) * T::BUF;
   // buffer (j+3)%4 held tile j-1, released by the barrier that ended iteration j-1
-  dma_tile<D>(smem + ((j + 3) % NBUF) * T::BUF, kp, vp, k_row, (j + 3) * BC, nk_load, dm);
+  dma_tile<D, F8>(smem + ((j + 3) % NBUF) * T::BUF, kp, vp, k_row, (j + 3) * BC, nk_load, dm);
   if (kv0 + BC > nk || (CAUSAL && kv0 + BC - 1 > q0)) mask_tile<CAUSAL>(s, kv0, nk, q0, l32, h);
 
   // Conditional rescaling (Lecture 21 notes §5.3): the reference m only moves when the tile's
@@ -250,7 +308,10 @@ __device__ __forceinline__ void tile_step(char* smem, int j, const uint16_t* kp,
   }
 
   // ---- phase A: scores of tile j+1 (MFMA) interleaved with the softmax of tile j (VALU) ----
-  if (NEXT) scores<D>(smem + ((j + 1) % NBUF) * T::BUF, krow0, h, qf, sn);
+  if constexpr (NEXT) {
+    if constexpr (F8) scores_f8<D>(smem + ((j + 1) % NBUF) * T::BUF, krow0, h, qf, sn);
+    else scores<D>(smem + ((j + 1) % NBUF) * T::BUF, krow0, h, qf, sn);
+  }
 #pragma unroll
   for (int qh = 0; qh < QH; ++qh)
 #pragma unroll
@@ -285,10 +346,9 @@ __device__ __forceinline__ void tile_step(char* smem, int j, const uint16_t* kp,
   wait_vm_barrier<T::VMCNT>();  // tile j+2 landed; tile j+3 may still be in flight
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
-  using T = Tile<D>;
-  __shared__ __attribute__((aligned(16))) char smem[NBUF * T::BUF];
+template <int D, bool CAUSAL, bool F8>
+__device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
+  using T = Tile<D, F8>;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5, l32 = lane & 31;
@@ -308,15 +368,33 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   const int b = bh / a.Hq, hq = bh % a.Hq, hk = hq / a.G;
 
   const uint16_t* qp = (const uint16_t*)a.q + (long)b * a.Nq * a.q_row + hq * D;
-  const uint16_t* kp = (const uint16_t*)a.k + (long)b * a.Nk * a.k_row + hk * D;
-  const uint16_t* vp = (const uint16_t*)a.v + (long)b * a.Nk * a.k_row + hk * D;
+  const char* kp = (const char*)a.k + ((long)b * a.Nk * a.k_row + hk * D) * T::KE;
+  const char* vp = (const char*)a.v + ((long)b * a.Nk * a.k_row + hk * D) * 2;
   const long q_valid = ((long)(a.Nq - 1) * a.q_row + D) * 2;
 
   const int q0 = qb * BR + wave * 32 * QH;  // first query row of this wave
 
-  // Q as the B operand of S^T = K Q^T: lane holds column q0 + 32qh + l32, dims [16ks + 8h, +8).
-  bf16x8 qf[QH][D / 16];
-  {
+  // Q as the B operand of S^T = K Q^T: lane holds column q0 + 32qh + l32, dims [16ks + 8h, +8)
+  // (bf16) or [64ks + 32h, +32) (E4M3).
+  typename QFrag<D, F8>::type qf;
+  float cw = a.c;             // scale * log2(e), times the Q block scale on the FP8 path
+  const float* ksc = nullptr;  // K block scales of this (batch, kv head), FP8 path
+  if constexpr (F8) {
+    const char* qp8 = (const char*)a.q + (long)b * a.Nq * a.q_row + hq * D;
+    const rsrc_t rq = make_rsrc(qp8, (long)(a.Nq - 1) * a.q_row + D);
+#pragma unroll
+    for (int qh = 0; qh < QH; ++qh)
+#pragma unroll
+      for (int ks = 0; ks < D / 64; ++ks) {
+        const int off = (int)((long)(q0 + 32 * qh + l32) * a.q_row + ks * 64 + h * 32);
+        const u32x4 lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+        const u32x4 hi = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16, 0, 0));
+        qf[qh][ks] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    // rows past N (last workgroup) take the last block's scale; their output is dropped
+    cw *= a.q_scale[((long)b * a.Hq + hq) * a.q_nblk + min(q0 / kFp8Block, a.q_nblk - 1)];
+    ksc = a.k_scale + ((long)b * a.Hkv + hk) * a.k_nblk;
+  } else {
     const rsrc_t rq = make_rsrc(qp, q_valid);
 #pragma unroll
     for (int qh = 0; qh < QH; ++qh)
@@ -349,40 +427,41 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   }
 
   // tiles 0, 1, 2 in flight; wait for 0 and 1 (the last tile's loads may stay outstanding)
-  TileDma<D> dm;
+  TileDma<D, F8> dm;
   dm.init(a.k_row);
-  dma_tile<D>(smem, kp, vp, a.k_row, 0, nk_load, dm);
-  dma_tile<D>(smem + T::BUF, kp, vp, a.k_row, BC, nk_load, dm);
-  dma_tile<D>(smem + 2 * T::BUF, kp, vp, a.k_row, 2 * BC, nk_load, dm);
+  dma_tile<D, F8>(smem, kp, vp, a.k_row, 0, nk_load, dm);
+  dma_tile<D, F8>(smem + T::BUF, kp, vp, a.k_row, BC, nk_load, dm);
+  dma_tile<D, F8>(smem + 2 * T::BUF, kp, vp, a.k_row, 2 * BC, nk_load, dm);
   wait_vm_barrier<T::VMCNT>();
 
   const int krow0 = swap_bits23(l32);
   // scores alternate between two register sets (the loop is unrolled by two tiles), so the
   // next tile's scores never need copying
   f32x16 s0[QH][2], s1[QH][2];
-  scores<D>(smem, krow0, h, qf, s0);
+  if constexpr (F8) scores_f8<D>(smem, krow0, h, qf, s0);
+  else scores<D>(smem, krow0, h, qf, s0);
 
   int j = 0;
   for (; j + 1 < last_w; j += 2) {
-    tile_step<D, CAUSAL, true>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, a.c, qf, s0, s1,
+    tile_step<D, CAUSAL, true, F8>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, qf, s0, s1,
                                o, m, l);
-    tile_step<D, CAUSAL, true>(smem, j + 1, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, a.c, qf, s1,
+    tile_step<D, CAUSAL, true, F8>(smem, j + 1, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, qf, s1,
                                s0, o, m, l);
   }
   if (j < last_w) {
-    tile_step<D, CAUSAL, true>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, a.c, qf, s0, s1,
+    tile_step<D, CAUSAL, true, F8>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, qf, s0, s1,
                                o, m, l);
     ++j;
-    tile_step<D, CAUSAL, false>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, a.c, qf, s1,
+    tile_step<D, CAUSAL, false, F8>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, qf, s1,
                                 s0, o, m, l);
   } else {
-    tile_step<D, CAUSAL, false>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, a.c, qf, s0,
+    tile_step<D, CAUSAL, false, F8>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, qf, s0,
                                 s1, o, m, l);
   }
   ++j;
   // tiles past this wave's diagonal: keep the workgroup's barrier count
   for (; j < n_tiles; ++j) {
-    dma_tile<D>(smem + ((j + 3) % NBUF) * T::BUF, kp, vp, a.k_row, (j + 3) * BC, nk_load, dm);
+    dma_tile<D, F8>(smem + ((j + 3) % NBUF) * T::BUF, kp, vp, a.k_row, (j + 3) * BC, nk_load, dm);
     wait_vm_barrier<T::VMCNT>();
   }
   __builtin_amdgcn_s_waitcnt(0);  // drain the tail prefetches before the workgroup ends
@@ -406,6 +485,22 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
       }
     if (h == 0 && qi < a.Nq) a.lse[((long)b * a.Hq + hq) * a.Nq + qi] = (m[qh] + __log2f(lt)) * kLn2;
   }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[NBUF * Tile<D>::BUF];
+  fwd_body<D, CAUSAL, false>(a, smem);
+}
+
+// FP8 path (Lecture 21 notes §4.4; "Flash Attention 3/4 笔记" §4): Q and K arrive as E4M3 codes
+// with one scale per 64-row block (after the random-sign Hadamard rotation, which cancels in
+// Q K^T); the score product runs on the FP8 MFMA at twice the bf16 rate and the block scales
+// fold into the per-tile softmax multiplier. P and V stay bf16.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[NBUF * Tile<D, true>::BUF];
+  fwd_body<D, CAUSAL, true>(a, smem);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -521,6 +616,14 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t s) {
     if (a.causal) hipLaunchKernelGGL((fwd_bf16_kernel<64, true>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((fwd_bf16_kernel<64, false>), grid, block, 0, s, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_fp8(const FwdArgs& a, int d, hipStream_t s) {
+  if (d != 128) return hipErrorInvalidValue;
+  const dim3 grid(a.n_tasks), block(kThreads);
+  if (a.causal) hipLaunchKernelGGL((fwd_fp8_kernel<128, true>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((fwd_fp8_kernel<128, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 

@@ -20,6 +20,10 @@ struct FwdArgs {
   int causal;
   int n_qblk;   // query blocks per (batch, head)
   int n_tasks;  // B * Hq * n_qblk
+  // FP8 (E4M3) Q and K only: one fp32 scale per 64-row block, [B, Hq, q_nblk] / [B, Hkv, k_nblk]
+  const float* q_scale;
+  const float* k_scale;
+  int q_nblk, k_nblk;
 };
 
 struct DecArgs {
@@ -61,7 +65,7 @@ struct BwdArgs {
 };
 
 // Planner constants shared by the host code and the kernels.
-constexpr int kFwdRows = 256;     // query rows per bf16 forward workgroup (4 waves x 64)
+constexpr int kFwdRows = 256;     // query rows per bf16 / fp8 forward workgroup (8 waves x 32)
 constexpr int kFwdF32Rows = 128;  // query rows per fp32 forward workgroup (4 waves x 32)
 constexpr int kFwdKeys = 64;      // keys per forward K/V tile
 constexpr int kFwdF32Keys = 32;   // keys per tile in the fp32 forward
@@ -73,6 +77,10 @@ constexpr int kBwdDqKeys = 64;    // keys per dQ K/V tile
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, hipStream_t s);
+hipError_t launch_fwd_fp8(const FwdArgs& a, int d, hipStream_t s);
+constexpr int kFp8Block = 64;     // rows per FP8 quantisation block (one scale each)
+hipError_t launch_quantize_fp8(const void* x, const float* signs, void* x8, float* scales, int B, int N, int H,
+                               int d, hipStream_t s);
 hipError_t launch_decode(const DecArgs& a, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t s);
 

@@ -92,6 +92,32 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int
               float* lse, int B, int Hq, int Hkv, int Nq, int Nk_max, int d, float scale, int dtype,
               void* workspace, size_t ws_bytes, void* stream);
 
+/* ---- FP8 forward (Lecture 21 notes §4.4 and exercise 8; "Flash Attention 3/4 笔记" §4) ----
+ * Q and K in OCP E4M3 (one byte per value) with one fp32 scale per 64-row block of each
+ * (batch, head), optionally rotated first by the same random orthogonal J = diag(signs) H_d /
+ * sqrt(d), which leaves Q K^T unchanged and spreads outliers over all dimensions. The score
+ * product runs on the FP8 MFMA; P and V stay bf16, O is bf16 and L fp32 as in fa_fwd. */
+
+/* Number of block scales fa_quantize_fp8 writes for a [B, N, H, d] tensor: B * H * ceil(N / 64). */
+size_t fa_fp8_scale_count(int B, int N, int H);
+
+/* x: bf16 [B, N, H, d] (d in {64, 128}). signs: d fp32 values of +1 or -1 on the device, or
+ * NULL for no rotation. x8: E4M3 codes [B, N, H, d]. scales: fp32 [B, H, ceil(N/64)].
+ * Row r of (b, h) is multiplied by signs, transformed by the fast Walsh-Hadamard transform
+ * and by 1/sqrt(d) (in fp32, in that order), then its block of 64 rows is scaled so the
+ * block's largest magnitude is 448 and rounded to nearest-even E4M3: code = round(y * 448 /
+ * amax), scale = amax / 448 (1 for an all-zero block); the value a code stands for is
+ * decode(code) * scale. Quantise Q and K with the same signs. x and x8 16-byte aligned. */
+int fa_quantize_fp8(const void* x, const float* signs, void* x8, float* scales, int B, int N, int H, int d,
+                    void* stream);
+
+/* Forward from E4M3 q8 [B,Nq,Hq,d] and k8 [B,Nk,Hkv,d] with their block scales (as written by
+ * fa_quantize_fp8) and bf16 v [B,Nk,Hkv,d]: the fa_fwd result for Q = decode(q8) * q_scale and
+ * K = decode(k8) * k_scale. d must be 128. o bf16 [B,Nq,Hq,d], lse fp32 [B,Hq,Nq]. */
+int fa_fwd_fp8(const void* q8, const void* k8, const void* v, const float* q_scale, const float* k_scale,
+               void* o, float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+               void* stream);
+
 /* Static text for a status code (for FA_ERR_HIP: the last HIP error seen by this thread). */
 const char* fa_strerror(int code);
 int fa_version(void);

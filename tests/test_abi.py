@@ -153,3 +153,22 @@ def test_decode_chunk_plan():
     for B, H, N in [(1, 1, 1), (3, 5, 77), (128, 8, 131072)]:
         c = fa.decode_chunk(B, H, N)
         assert c % 256 == 0 and 256 <= c <= 2048
+
+
+def test_fp8_validation_and_scale_count():
+    L = fa.lib()
+    assert L.fa_fp8_scale_count(2, 130, 3) == 2 * 3 * 3
+    assert L.fa_fp8_scale_count(0, 130, 3) == 0
+    q = lambda **kw: L.fa_quantize_fp8(kw.get("x", P), kw.get("signs", None), kw.get("x8", P), kw.get("sc", P),  # noqa: E731
+                                       kw.get("B", 1), kw.get("N", 8), kw.get("H", 1), kw.get("d", 128), None)
+    assert q(x=None) == INVALID and q(sc=None) == INVALID and q(x8=MIS) == INVALID and q(signs=MIS) == INVALID
+    assert q(N=0) == INVALID and q(d=96) == UNSUPPORTED
+
+    def f(**kw):
+        a = dict(q8=P, k8=P, v=P, qs=P, ks=P, o=P, lse=P, B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=128, causal=0, scale=0.1)
+        a.update(kw)
+        return L.fa_fwd_fp8(a["q8"], a["k8"], a["v"], a["qs"], a["ks"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                            a["Nq"], a["Nk"], a["d"], a["causal"], a["scale"], None)
+    assert f(qs=None) == INVALID and f(ks=None) == INVALID and f(k8=None) == INVALID
+    assert f(d=64) == UNSUPPORTED  # the FP8 forward is built for d = 128
+    assert f(causal=1, Nk=9) == UNSUPPORTED and f(Hq=3, Hkv=2) == INVALID and f(scale=0.0) == INVALID
