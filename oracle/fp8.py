@@ -19,9 +19,10 @@ Readings where the pages are silent (listed in the design notes as well):
     NaN), rounding is to nearest with ties to even, and values are clamped to +-448 first;
   * J = diag(signs) H_d / sqrt(d): the signs multiply first, then the (Sylvester, natural
     order) Hadamard transform, then 1/sqrt(d);
-  * a block is 64 consecutive rows of one (batch, head); its scale is amax / 448, so the
-    block's largest magnitude maps to 448 exactly (an all-zero block gets scale 1);
-  * the rotation, the scale and the division are done in fp32 in a fixed order (the
+  * a block is 64 consecutive rows of one (batch, head); its scale is amax / 448 and its
+    values are multiplied by 448 / amax (both fp32, correctly rounded) before rounding, so
+    the block's largest magnitude maps to 448 (an all-zero block gets scale 1);
+  * the rotation, the scale and the multiplication are done in fp32 in a fixed order (the
     butterfly stages h = 1, 2, 4, ..., d/2 with (a, b) -> (a + b, a - b)), because the code
     is an integer decided by floating point: the GPU makes the same decisions in fp32.
 """
@@ -119,8 +120,10 @@ def quantize(x, signs=None, block: int = BLOCK_ROWS):
         blk = y[:, r0:r1]  # [B, rows, H, d]
         amax = np.abs(blk).max(axis=(1, 3))  # [B, H]
         sc = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+        safe = np.where(amax > 0, amax, np.float32(1.0)).astype(np.float32)
+        inv = np.where(amax > 0, np.float32(E4M3_MAX) / safe, np.float32(1.0)).astype(np.float32)
         scales[:, :, i] = sc
-        q = (blk / sc[:, None, :, None]).astype(np.float32)
+        q = (blk * inv[:, None, :, None]).astype(np.float32)
         q = np.clip(q, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
         codes[:, r0:r1] = round_e4m3(q)
     rows = np.arange(N) // block
