@@ -32,6 +32,9 @@ import workloads  # noqa: E402
 
 METRIC = "attn fwd/bwd TFLOPS & % bf16 MFMA peak (d=128); decode HBM GB/s"
 PEAK_BF16_TFLOPS = 2516.6  # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense fp8 MFMA
+# the FP8 path runs Q K^T (half the FLOPs) on fp8 MFMA and P V on bf16 MFMA
+PEAK_FP8_QK_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
 PEAK_HBM_GBS = 8000.0
 
 
@@ -274,6 +277,33 @@ def main():
                                                 "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                                                 "tflops_8n2d_convention": round(0.8 * tf, 2)}
         del q, k, v, do, o, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+
+        # FP8 forward on the training shape: Q and K quantised to E4M3 beforehand (as the kernel
+        # producing them would hand them over), so the timed call is the attention alone; the
+        # quantise pass is timed on its own (HBM bound: 2 bytes read, 1 written per value)
+        log("[bench] fwd_fp8_b16h16n2048d128")
+        inp = workloads.make_attention_inputs(w.B, w.Nq, w.Nk, w.Hq, w.Hkv, w.d, w.seed, w.dtype)
+        q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+        del inp
+        signs = np.random.Generator(np.random.PCG64(9)).choice([-1.0, 1.0], size=w.d).astype(np.float32)
+        signs = torch.from_numpy(signs).cuda()
+        q8, qs = fa.quantize_fp8(q, signs)
+        k8, ks = fa.quantize_fp8(k, signs)
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda")
+        for m in (False, True):
+            ms = float(np.mean(time_launches(
+                lambda: fa.fa_fwd_fp8(q8, k8, v, qs, ks, o, lse, causal=m, scale=w.scale), args.reps * 2, 3)))
+            tf = ff[m] / (ms * 1e-3) / 1e12
+            results["fwd_fp8_%s_b16h16n2048d128" % ("causal" if m else "nc")] = {
+                "ms": round(ms, 4), "tflops": round(tf, 2), "peak": round(PEAK_FP8_QK_TFLOPS, 1),
+                "frac_peak": round(tf / PEAK_FP8_QK_TFLOPS, 4)}
+        ms = float(np.mean(time_launches(lambda: fa.fa_quantize_fp8(q, signs, q8, qs), args.reps, 2)))
+        qbytes = q.numel() * 3 + qs.numel() * 4
+        results["quantize_fp8_b16h16n2048d128"] = {"ms": round(ms, 4), "gbs": round(qbytes / (ms * 1e-3) / 1e9, 1),
+                                                   "frac_hbm": round(qbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        del q, k, v, q8, k8, qs, ks, o, lse, signs
         torch.cuda.empty_cache()
 
     line = {
