@@ -23,7 +23,7 @@ _STATUS = {0: "FA_OK", -1: "FA_ERR_INVALID_ARG", -2: "FA_ERR_UNSUPPORTED", -3: "
 EXPORTED = (
     "fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_workspace_size", "fa_strerror",
     "fa_version", "fa_wave_efficiency", "fa_plan_splits", "fa_schedule_makespan", "fa_causal_tiles",
-    "fa_decode_chunk", "fa_fp8_scale_count", "fa_quantize_fp8", "fa_fwd_fp8",
+    "fa_decode_chunk", "fa_fp8_scale_count", "fa_quantize_fp8", "fa_fwd_fp8", "fa_fwd_dropout", "fa_bwd_dropout",
 )
 
 _lib = None
@@ -73,6 +73,11 @@ def lib() -> ctypes.CDLL:
     L.fa_quantize_fp8.restype = i
     L.fa_fwd_fp8.argtypes = [vp] * 7 + [i] * 7 + [f, vp]
     L.fa_fwd_fp8.restype = i
+    u64, u32 = ctypes.c_ulonglong, ctypes.c_uint
+    L.fa_fwd_dropout.argtypes = [vp] * 5 + [i] * 7 + [f, f, u64, u32, vp]
+    L.fa_fwd_dropout.restype = i
+    L.fa_bwd_dropout.argtypes = [vp] * 9 + [i] * 7 + [f, f, u64, u32, vp, sz, vp]
+    L.fa_bwd_dropout.restype = i
     _lib = L
     return L
 
@@ -163,6 +168,29 @@ def fa_fwd_fp8(q8, k8, v, q_scale, k_scale, o, lse, causal: bool = False, scale:
                             Hkv, Nq, Nk, d, int(causal), scale, _stream(stream)))
 
 
+def fa_fwd_dropout(q, k, v, o, lse, p: float, seed: int, offset: int = 0, causal: bool = False,
+                   scale: float | None = None, stream=None) -> None:
+    """The forward with dropout probability p on P (bf16; see include/fa.h)."""
+    _need_contig(q, k, v, o, lse)
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    _check(lib().fa_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, int(causal),
+                                scale, p, seed, offset, _stream(stream)))
+
+
+def fa_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, workspace, p: float, seed: int, offset: int = 0,
+                   causal: bool = False, scale: float | None = None, stream=None) -> None:
+    _need_contig(q, k, v, o, dout, lse, dq, dk, dv, workspace)
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().fa_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                                _ptr(dv), B, Hq, Hkv, Nq, Nk, d, int(causal), scale, p, seed, offset,
+                                _ptr(workspace), ws_bytes, _stream(stream)))
+
+
 def fa_bwd_workspace_size(B: int, Hq: int, Nq: int, d: int) -> int:
     return int(lib().fa_bwd_workspace_size(B, Hq, Nq, d))
 
@@ -202,6 +230,28 @@ def decode(q, k_cache, v_cache, seqlens, scale: float | None = None, stream=None
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     fa_decode(q, k_cache, v_cache, seqlens, o, lse, ws, scale, stream)
     return o, lse
+
+
+def forward_dropout(q, k, v, p: float, seed: int, offset: int = 0, causal: bool = False,
+                    scale: float | None = None, stream=None):
+    import torch
+
+    B, Nq, Hq, _ = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    fa_fwd_dropout(q, k, v, o, lse, p, seed, offset, causal, scale, stream)
+    return o, lse
+
+
+def backward_dropout(q, k, v, o, dout, lse, p: float, seed: int, offset: int = 0, causal: bool = False,
+                     scale: float | None = None, stream=None):
+    import torch
+
+    B, Nq, Hq, d = q.shape
+    ws = torch.empty(fa_bwd_workspace_size(B, Hq, Nq, d), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fa_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, ws, p, seed, offset, causal, scale, stream)
+    return dq, dk, dv
 
 
 def quantize_fp8(x, signs=None, stream=None):

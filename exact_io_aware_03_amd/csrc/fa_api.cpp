@@ -36,6 +36,17 @@ int common_checks(int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale) {
   return FA_OK;
 }
 
+// Dropout parameters: p must lie in [0, 1); it is used at 1/256 resolution (threshold t).
+int make_dropout(float p, unsigned long long seed, unsigned int offset, fa::Dropout& dp) {
+  if (!std::isfinite(p) || p < 0.f || p >= 1.f) return FA_ERR_INVALID_ARG;
+  dp.t = (uint32_t)std::min(255.0, std::floor(256.0 * (double)p));
+  dp.scale = (float)(256.0 / (256.0 - (double)dp.t));
+  dp.k0 = (uint32_t)(seed & 0xffffffffull);
+  dp.k1 = (uint32_t)(seed >> 32);
+  dp.offset = offset;
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -53,8 +64,9 @@ const char* fa_strerror(int code) {
   }
 }
 
-int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Nq,
-           int Nk, int d, int causal, float scale, int dtype, void* stream) {
+static int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                      int Nq, int Nk, int d, int causal, float scale, int dtype, const fa::Dropout* drop,
+                      void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_INVALID_ARG;
   int st = common_checks(B, Hq, Hkv, Nq, Nk, d, scale);
@@ -77,7 +89,25 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   if (tasks > INT_MAX) return FA_ERR_INVALID_ARG;
   a.n_tasks = (int)tasks;
   hipStream_t s = (hipStream_t)stream;
+  if (drop && drop->t > 0) {
+    a.drop = *drop;
+    return hip_status(fa::launch_fwd_dropout(a, d, s));
+  }
   return hip_status(dtype == FA_BF16 ? fa::launch_fwd_bf16(a, d, s) : fa::launch_fwd_f32(a, d, s));
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Nq,
+           int Nk, int d, int causal, float scale, int dtype, void* stream) {
+  return fwd_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, dtype, nullptr, stream);
+}
+
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Nq,
+                   int Nk, int d, int causal, float scale, float p_drop, unsigned long long seed, unsigned int offset,
+                   void* stream) {
+  fa::Dropout dp{};
+  const int st = make_dropout(p_drop, seed, offset, dp);
+  if (st != FA_OK) return st;
+  return fwd_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, FA_BF16, &dp, stream);
 }
 
 size_t fa_fp8_scale_count(int B, int N, int H) {
@@ -129,9 +159,10 @@ size_t fa_bwd_workspace_size(int B, int Hq, int Nq, int d) {
   return align256((size_t)B * Hq * Nq * sizeof(float));  // D = rowsum(dO * O)
 }
 
-int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
-           void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
-           int dtype, void* workspace, size_t ws_bytes, void* stream) {
+static int bwd_common(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                      void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                      float scale, int dtype, void* workspace, size_t ws_bytes, const fa::Dropout* drop,
+                      void* stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
   for (const void* p : {q, k, v, o, dout, (const void*)lse, (const void*)dq, (const void*)dk, (const void*)dv})
     if (!aligned16(p)) return FA_ERR_INVALID_ARG;
@@ -159,7 +190,29 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   if (tasks > INT_MAX || tasks_dq > INT_MAX || (long)B * Nq * Hq > INT_MAX / 4) return FA_ERR_INVALID_ARG;
   a.n_tasks = (int)tasks;
   a.n_tasks_dq = (int)tasks_dq;
+  if (drop && drop->t > 0) {
+    a.drop = *drop;
+    return hip_status(fa::launch_bwd_dropout(a, d, (hipStream_t)stream));
+  }
   return hip_status(fa::launch_bwd(a, d, (hipStream_t)stream));
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+           void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+           int dtype, void* workspace, size_t ws_bytes, void* stream) {
+  return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, causal, scale, dtype, workspace,
+                    ws_bytes, nullptr, stream);
+}
+
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                   void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                   float scale, float p_drop, unsigned long long seed, unsigned int offset, void* workspace,
+                   size_t ws_bytes, void* stream) {
+  fa::Dropout dp{};
+  const int st = make_dropout(p_drop, seed, offset, dp);
+  if (st != FA_OK) return st;
+  return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, causal, scale, FA_BF16, workspace,
+                    ws_bytes, &dp, stream);
 }
 
 int fa_decode_chunk(int B, int Hkv, int Nk_max) {

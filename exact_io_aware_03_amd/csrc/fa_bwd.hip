@@ -203,7 +203,9 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a) {
   }
 }
 
-template <int D>
+// DROP: the forward's dropout on P (Lecture 21 notes §2.8, exercise 4), its mask regenerated:
+// dV takes P * Z / (1 - p), dP = (dO V^T) * Z / (1 - p), and D = rowsum(dO * O) still holds.
+template <int D, bool DROP>
 __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(BwdArgs a) {
   using L = BwdLds<D>;
   constexpr int KS = D / 16, DB = D / 32;
@@ -321,6 +323,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(BwdArgs a) {
     }
     // register i holds query row 32qhalf + (i&7) + 8h + 16(i>>3) and key `key`
     const int qw0 = q0 + 32 * qhalf;  // first row of this wave's half
+    const int bhq = b * a.Hq + hk * a.G + st / per_head;  // (batch, query head) of this step
     if (kw0 + 31 >= a.Nk || (a.causal && kw0 + 31 > qw0)) {
       // key past the end: every row masked; causal: rows before the key masked
       const int first_row = key >= a.Nk ? 0x7fffffff : (a.causal ? key : 0);
@@ -335,13 +338,24 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(BwdArgs a) {
       const int lo = lb + BUF * BQ * 4 + 64 * hi;
       const f32x4 la = ld4f(lo), lbv = ld4f(lo + 16);
       const f32x4 da = ld4f(lo + 2 * BQ * 4), dbv = ld4f(lo + 2 * BQ * 4 + 16);
+      uint32_t keep = 0xff;
+      if constexpr (DROP) {  // rows qw0 + 16hi + 8h .. +7 of this lane's key
+        const int rg = (qw0 + 16 * hi + 8 * h) >> 2;
+        keep = drop_rows4(a.drop, key, rg, bhq) | (drop_rows4(a.drop, key, rg + 1, bhq) << 4);
+      }
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
         const int i = 8 * hi + x;
         const float lv = x < 4 ? la[x] : lbv[x - 4], dvv = x < 4 ? da[x] : dbv[x - 4];
         const float p = fast_exp2(fmaf(s[i], a.c, -lv * kLog2e));
-        s[i] = p;                  // P
-        g[i] = p * (g[i] - dvv);  // dS
+        if constexpr (DROP) {
+          const bool z = (keep >> x) & 1;
+          s[i] = z ? p * a.drop.scale : 0.f;                   // P Z / (1 - p)
+          g[i] = p * ((z ? g[i] * a.drop.scale : 0.f) - dvv);  // dS
+        } else {
+          s[i] = p;                  // P
+          g[i] = p * (g[i] - dvv);  // dS
+        }
       }
     }
     // ---- dV += P^T dO, dK += dS^T Q over this wave's 32 rows (16 per product) ----
@@ -434,7 +448,7 @@ __device__ __forceinline__ void dq_dma_tile(char* buf, const uint16_t* kp, const
   dma_rows<D, T::DMA>(buf + T::T_BYTES, vp + (long)kv0 * k_row, k_row, nk - kv0);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(kMainThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   using T = DqTile<D>;
   constexpr int KS = D / 16, DB = D / 32;
@@ -565,9 +579,19 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(fmaf(s[kb][i], a.c, -l2));
-        g[kb][i] = p * (g[kb][i] - dd);  // dS
+      for (int hi = 0; hi < 2; ++hi) {
+        uint32_t keep = 0xff;
+        if constexpr (DROP) {  // keys kv0 + 32kb + 16hi + 8h .. +7 of row qi
+          const int kg = (kv0 + 32 * kb + 16 * hi + 8 * h) >> 2;
+          keep = drop_keys4(a.drop, kg, qi, bh) | (drop_keys4(a.drop, kg + 1, qi, bh) << 4);
+        }
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const int i = 8 * hi + x;
+          const float p = fast_exp2(fmaf(s[kb][i], a.c, -l2));
+          if constexpr (DROP) g[kb][i] = p * (((keep >> x) & 1 ? g[kb][i] * a.drop.scale : 0.f) - dd);  // dS
+          else g[kb][i] = p * (g[kb][i] - dd);                                                        // dS
+        }
       }
     // ---- dQ^T += K^T dS^T: 16-key step kk takes dS registers 8(kk&1) .. +7 of block kk/2 ----
 #pragma unroll
@@ -608,25 +632,29 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dq_kernel(BwdArgs a) {
     }
 }
 
-template <int D>
+template <int D, bool DROP>
 hipError_t launch_d(const BwdArgs& a, hipStream_t s) {
   const long rows = (long)a.B * a.Nq * a.Hq, rows_per_block = kThreads / (D / 8);
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((rows + rows_per_block - 1) / rows_per_block), dim3(kThreads), 0, s,
                      a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_main_kernel<D>), dim3(a.n_tasks), dim3(kMainThreads), 0, s, a);
+  hipLaunchKernelGGL((bwd_main_kernel<D, DROP>), dim3(a.n_tasks), dim3(kMainThreads), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3(a.n_tasks_dq), dim3(kMainThreads), 0, s, a);
-  else hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3(a.n_tasks_dq), dim3(kMainThreads), 0, s, a);
+  if (a.causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true, DROP>), dim3(a.n_tasks_dq), dim3(kMainThreads), 0, s, a);
+  else hipLaunchKernelGGL((bwd_dq_kernel<D, false, DROP>), dim3(a.n_tasks_dq), dim3(kMainThreads), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t s) {
-  return d == 128 ? launch_d<128>(a, s) : launch_d<64>(a, s);
+  return d == 128 ? launch_d<128, false>(a, s) : launch_d<64, false>(a, s);
+}
+
+hipError_t launch_bwd_dropout(const BwdArgs& a, int d, hipStream_t s) {
+  return d == 128 ? launch_d<128, true>(a, s) : launch_d<64, true>(a, s);
 }
 
 }  // namespace fa

@@ -14,6 +14,7 @@
 // that freedom to hand the softmax output straight from the accumulator registers to the
 // next product without a trip through LDS.
 #pragma once
+#include "fa_internal.h"
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -125,5 +126,47 @@ __device__ __forceinline__ int swap_bits23(int r) {
 // XOR swizzle of 16-byte chunks for row-major LDS tiles read 32 rows at a time through the
 // relabelling above: the 8 rows any 8 consecutive lanes touch land in 8 distinct chunks.
 __device__ __forceinline__ int swz_perm_rows(int row) { return (row & 3) | ((row >> 1) & 4); }
+
+// ---- dropout mask (Lecture 21 notes §2.8: regenerate the mask from the seed) ----
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3",
+// SC'11): ten rounds of (c0, c1, c2, c3) -> (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1,
+// lo(M0 c0)) with the key advanced by the Weyl increments after every round.
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+    c = u32x4{(uint32_t)(p1 >> 32) ^ c[1] ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c[3] ^ k1, (uint32_t)p0};
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+// One Philox call covers the 4 x 4 block of (row, key) positions (4 rg .. +3, 4 kg .. +3) of
+// one (batch, query head) `bh`: counter (kg, rg, bh, offset), key (k0, k1); word r holds row
+// 4 rg + r, byte c (little-endian) key 4 kg + c; a position is kept when its byte is >= t, and
+// kept probabilities are multiplied by 256 / (256 - t).
+__device__ __forceinline__ u32x4 drop_block(const Dropout& dp, int kg, int rg, int bh) {
+  return philox4x32_10(u32x4{(uint32_t)kg, (uint32_t)rg, (uint32_t)bh, dp.offset}, dp.k0, dp.k1);
+}
+// bit c set when byte c of x is kept
+__device__ __forceinline__ uint32_t drop_bits(const Dropout& dp, uint32_t x) {
+  return ((x & 255u) >= dp.t ? 1u : 0u) | (((x >> 8) & 255u) >= dp.t ? 2u : 0u) |
+         (((x >> 16) & 255u) >= dp.t ? 4u : 0u) | ((x >> 24) >= dp.t ? 8u : 0u);
+}
+// keep mask (bit c) of the 4 keys 4 kg .. +3 in row `row`
+__device__ __forceinline__ uint32_t drop_keys4(const Dropout& dp, int kg, int row, int bh) {
+  const u32x4 w = drop_block(dp, kg, row >> 2, bh);
+  const int r = row & 3;
+  return drop_bits(dp, r == 0 ? w[0] : r == 1 ? w[1] : r == 2 ? w[2] : w[3]);
+}
+// keep mask (bit r) of the 4 rows 4 rg .. +3 for key `key`
+__device__ __forceinline__ uint32_t drop_rows4(const Dropout& dp, int key, int rg, int bh) {
+  const u32x4 w = drop_block(dp, key >> 2, rg, bh);
+  const int sh = 8 * (key & 3);
+  return (((w[0] >> sh) & 255u) >= dp.t ? 1u : 0u) | (((w[1] >> sh) & 255u) >= dp.t ? 2u : 0u) |
+         (((w[2] >> sh) & 255u) >= dp.t ? 4u : 0u) | (((w[3] >> sh) & 255u) >= dp.t ? 8u : 0u);
+}
 
 }  // namespace fa

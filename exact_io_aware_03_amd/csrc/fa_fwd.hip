@@ -266,10 +266,10 @@ __device__ __forceinline__ bf16x8 v_frag(const char* vt, int ks, int db, int lan
 // of tile j; with NEXT, the scores of tile j+1 are produced into s on exit.
 // c: scale * log2(e) (times this wave's Q block scale on the FP8 path); kscale: the FP8 path's
 // per-tile K block scales.
-template <int D, bool CAUSAL, bool NEXT, bool F8>
+template <int D, bool CAUSAL, bool NEXT, bool F8, bool DROP>
 __device__ __forceinline__ void tile_step(char* smem, int j, const char* kp, const char* vp, long k_row, int nk_load,
                                           int nk, const TileDma<D, F8>& dm, int q0, int l32, int h, int lane,
-                                          int krow0, float c_in, const float* kscale,
+                                          int krow0, float c_in, const float* kscale, const Dropout& dp, int bh,
                                           const typename QFrag<D, F8>::type& qf, f32x16 (&s)[QH][2],
                                           f32x16 (&sn)[QH][2], f32x16 (&o)[QH][D / 32], float (&m)[QH],
                                           float (&l)[QH]) {
@@ -327,10 +327,22 @@ __device__ __forceinline__ void tile_step(char* smem, int j, const char* kp, con
       const f32x16& sv = s[qh][ks >> 1];
       const int e = (ks & 1) * 8;
       u32x4 pw;
-      pw[0] = pack_bf16x2(sv[e + 0], sv[e + 1]);
-      pw[1] = pack_bf16x2(sv[e + 2], sv[e + 3]);
-      pw[2] = pack_bf16x2(sv[e + 4], sv[e + 5]);
-      pw[3] = pack_bf16x2(sv[e + 6], sv[e + 7]);
+      if constexpr (DROP) {
+        // dropout on P (§2.8): this lane's 8 keys kv0 + 16ks + 8h .. +7 of row q0 + 32qh + l32;
+        // the row sum l keeps the undropped values
+        const int qi = q0 + 32 * qh + l32, kg = (kv0 + 16 * ks + 8 * h) >> 2;
+        const uint32_t keep = drop_keys4(dp, kg, qi, bh) | (drop_keys4(dp, kg + 1, qi, bh) << 4);
+        float pd[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) pd[x] = (keep >> x) & 1 ? sv[e + x] * dp.scale : 0.f;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) pw[x] = pack_bf16x2(pd[2 * x], pd[2 * x + 1]);
+      } else {
+        pw[0] = pack_bf16x2(sv[e + 0], sv[e + 1]);
+        pw[1] = pack_bf16x2(sv[e + 2], sv[e + 3]);
+        pw[2] = pack_bf16x2(sv[e + 4], sv[e + 5]);
+        pw[3] = pack_bf16x2(sv[e + 6], sv[e + 7]);
+      }
       pf[qh] = as_bf16x8(pw);
     }
 #pragma unroll
@@ -346,7 +358,7 @@ __device__ __forceinline__ void tile_step(char* smem, int j, const char* kp, con
   wait_vm_barrier<T::VMCNT>();  // tile j+2 landed; tile j+3 may still be in flight
 }
 
-template <int D, bool CAUSAL, bool F8>
+template <int D, bool CAUSAL, bool F8, bool DROP>
 __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   using T = Tile<D, F8>;
 
@@ -443,19 +455,19 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
 
   int j = 0;
   for (; j + 1 < last_w; j += 2) {
-    tile_step<D, CAUSAL, true, F8>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, qf, s0, s1,
+    tile_step<D, CAUSAL, true, F8, DROP>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, a.drop, bh, qf, s0, s1,
                                o, m, l);
-    tile_step<D, CAUSAL, true, F8>(smem, j + 1, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, qf, s1,
+    tile_step<D, CAUSAL, true, F8, DROP>(smem, j + 1, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, a.drop, bh, qf, s1,
                                s0, o, m, l);
   }
   if (j < last_w) {
-    tile_step<D, CAUSAL, true, F8>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, qf, s0, s1,
+    tile_step<D, CAUSAL, true, F8, DROP>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, a.drop, bh, qf, s0, s1,
                                o, m, l);
     ++j;
-    tile_step<D, CAUSAL, false, F8>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, qf, s1,
+    tile_step<D, CAUSAL, false, F8, DROP>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, a.drop, bh, qf, s1,
                                 s0, o, m, l);
   } else {
-    tile_step<D, CAUSAL, false, F8>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, qf, s0,
+    tile_step<D, CAUSAL, false, F8, DROP>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, a.drop, bh, qf, s0,
                                 s1, o, m, l);
   }
   ++j;
@@ -490,17 +502,25 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[NBUF * Tile<D>::BUF];
-  fwd_body<D, CAUSAL, false>(a, smem);
+  fwd_body<D, CAUSAL, false, false>(a, smem);
 }
 
 // FP8 path (Lecture 21 notes §4.4; "Flash Attention 3/4 笔记" §4): Q and K arrive as E4M3 codes
 // with one scale per 64-row block (after the random-sign Hadamard rotation, which cancels in
 // Q K^T); the score product runs on the FP8 MFMA at twice the bf16 rate and the block scales
 // fold into the per-tile softmax multiplier. P and V stay bf16.
+// Dropout on P (Lecture 21 notes §2.8): the keep mask of every (row, key) is regenerated from
+// (seed, offset, batch, head, row, key) with Philox, one call per 4 x 4 block of positions.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void fwd_drop_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[NBUF * Tile<D>::BUF];
+  fwd_body<D, CAUSAL, false, true>(a, smem);
+}
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[NBUF * Tile<D, true>::BUF];
-  fwd_body<D, CAUSAL, true>(a, smem);
+  fwd_body<D, CAUSAL, true, false>(a, smem);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -615,6 +635,18 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t s) {
   } else {
     if (a.causal) hipLaunchKernelGGL((fwd_bf16_kernel<64, true>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((fwd_bf16_kernel<64, false>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_dropout(const FwdArgs& a, int d, hipStream_t s) {
+  const dim3 grid(a.n_tasks), block(kThreads);
+  if (d == 128) {
+    if (a.causal) hipLaunchKernelGGL((fwd_drop_kernel<128, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((fwd_drop_kernel<128, false>), grid, block, 0, s, a);
+  } else {
+    if (a.causal) hipLaunchKernelGGL((fwd_drop_kernel<64, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((fwd_drop_kernel<64, false>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }

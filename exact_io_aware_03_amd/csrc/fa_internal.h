@@ -4,8 +4,17 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace fa {
+
+// Dropout on the probabilities (mask regenerated from the seed; see fa_device.h).
+struct Dropout {
+  uint32_t k0, k1;  // Philox key: the seed's low and high words
+  uint32_t offset;  // fourth counter word (a fresh mask per call)
+  uint32_t t;       // byte threshold: a position is kept when its random byte is >= t
+  float scale;      // 256 / (256 - t)
+};
 
 struct FwdArgs {
   const void* q;
@@ -24,6 +33,7 @@ struct FwdArgs {
   const float* q_scale;
   const float* k_scale;
   int q_nblk, k_nblk;
+  Dropout drop;  // dropout on P (bf16 path): threshold t > 0 selects the dropout instance
 };
 
 struct DecArgs {
@@ -62,6 +72,7 @@ struct BwdArgs {
   int n_tasks;     // dK/dV kernel: B * Hkv * n_kvblk
   int n_qblk_dq;   // dQ kernel: query blocks per (batch, head)
   int n_tasks_dq;  // B * Hq * n_qblk_dq
+  Dropout drop;    // the forward's dropout, regenerated (t > 0 selects the dropout instance)
 };
 
 // Planner constants shared by the host code and the kernels.
@@ -78,6 +89,8 @@ constexpr int kBwdDqKeys = 64;    // keys per dQ K/V tile
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, hipStream_t s);
 hipError_t launch_fwd_fp8(const FwdArgs& a, int d, hipStream_t s);
+hipError_t launch_fwd_dropout(const FwdArgs& a, int d, hipStream_t s);
+hipError_t launch_bwd_dropout(const BwdArgs& a, int d, hipStream_t s);
 constexpr int kFp8Block = 64;     // rows per FP8 quantisation block (one scale each)
 hipError_t launch_quantize_fp8(const void* x, const float* signs, void* x8, float* scales, int B, int N, int H,
                                int d, hipStream_t s);

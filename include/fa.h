@@ -77,6 +77,23 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
            float scale, int dtype, void* workspace, size_t ws_bytes, void* stream);
 
+/* ---- dropout on the probabilities (Lecture 21 notes §2.8, exercise 4) ----
+ * O = (P * Z / (1 - p)) V with P the normalised probabilities; lse is still the logsumexp of the
+ * scores without dropout. Only the seed is kept: the keep mask Z is regenerated wherever it is
+ * needed from Philox4x32-10 (Salmon et al., SC'11), one call per 4 x 4 block of (row, key)
+ * positions of a (batch, query head): counter (key / 4, row / 4, b * Hq + h, offset), key (seed
+ * low word, seed high word); word row % 4, byte key % 4 (little-endian) is the position's random
+ * byte, kept when >= t = floor(256 p). Kept values are scaled by 256 / (256 - t), i.e. p is used
+ * at 1/256 resolution. p in [0, 1) (else FA_ERR_INVALID_ARG); p < 1/256 is no dropout. bf16 only,
+ * d in {64, 128}. The backward must get the forward's p, seed and offset. */
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Nq,
+                   int Nk, int d, int causal, float scale, float p_drop, unsigned long long seed, unsigned int offset,
+                   void* stream);
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                   void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                   float scale, float p_drop, unsigned long long seed, unsigned int offset, void* workspace,
+                   size_t ws_bytes, void* stream);
+
 /* Workspace bytes fa_decode needs: split-KV partials for up to ceil(Nk_max/256) splits. */
 size_t fa_decode_workspace_size(int B, int Hq, int Nk_max, int d);
 

@@ -57,20 +57,25 @@ def threshold(p: float) -> int:
     return min(255, int(np.floor(256.0 * p)))
 
 
-def keep_mask(B: int, Hq: int, Nq: int, Nk: int, p: float, seed: int, offset: int) -> np.ndarray:
-    """Z [B, Hq, Nq, Nk] (bool): the kept positions, from one Philox call per 4 x 4 block."""
+def keep_mask_head(bh: int, Nq: int, Nk: int, p: float, seed: int, offset: int) -> np.ndarray:
+    """Z [Nq, Nk] (bool) of one (batch, query head) with index bh = b * H_q + h."""
     t = threshold(p)
     key = (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
     nr, nc = (Nq + 3) // 4, (Nk + 3) // 4
     rg, cg = np.meshgrid(np.arange(nr), np.arange(nc), indexing="ij")
-    z = np.zeros((B, Hq, nr * 4, nc * 4), dtype=bool)
+    ctr = np.stack([cg, rg, np.full_like(rg, bh), np.full_like(rg, offset & 0xFFFFFFFF)], axis=-1)
+    words = philox4x32_10(ctr, key)  # [nr, nc, 4]: word r = row 4 rg + r
+    by = words[..., None].view(np.uint8).reshape(nr, nc, 4, 4)  # [.., row % 4, key % 4], little-endian
+    return (by >= t).transpose(0, 2, 1, 3).reshape(nr * 4, nc * 4)[:Nq, :Nk]
+
+
+def keep_mask(B: int, Hq: int, Nq: int, Nk: int, p: float, seed: int, offset: int) -> np.ndarray:
+    """Z [B, Hq, Nq, Nk] (bool): the kept positions, from one Philox call per 4 x 4 block."""
+    z = np.zeros((B, Hq, Nq, Nk), dtype=bool)
     for b in range(B):
         for h in range(Hq):
-            ctr = np.stack([cg, rg, np.full_like(rg, b * Hq + h), np.full_like(rg, offset & 0xFFFFFFFF)], axis=-1)
-            words = philox4x32_10(ctr, key)  # [nr, nc, 4]: word r = row 4 rg + r
-            by = words[..., None].view(np.uint8).reshape(nr, nc, 4, 4)  # [.., row%4, key%4], little-endian
-            z[b, h] = (by >= t).transpose(0, 2, 1, 3).reshape(nr * 4, nc * 4)
-    return z[:, :, :Nq, :Nk]
+            z[b, h] = keep_mask_head(b * Hq + h, Nq, Nk, p, seed, offset)
+    return z
 
 
 def _heads(B, Hq, Hkv):
