@@ -331,6 +331,9 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = (i & 7) + 16 * (i >> 3) < thr ? kNegInf : s[i];
     }
+    // dropout: keep bit 8hi + x of row qw0 + 16hi + 8h + x for this lane's key
+    uint32_t keep16 = 0xffff;
+    if constexpr (DROP) keep16 = drop_tile_rows(a.drop, (qw0 + 8 * h) >> 2, key, bhq);
     // P = exp(scale S - L), dS = P (dP - D); the 8 rows (i&7) are consecutive, so L and D
     // come in as 16-byte LDS reads
 #pragma unroll
@@ -338,11 +341,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(BwdArgs a) {
       const int lo = lb + BUF * BQ * 4 + 64 * hi;
       const f32x4 la = ld4f(lo), lbv = ld4f(lo + 16);
       const f32x4 da = ld4f(lo + 2 * BQ * 4), dbv = ld4f(lo + 2 * BQ * 4 + 16);
-      uint32_t keep = 0xff;
-      if constexpr (DROP) {  // rows qw0 + 16hi + 8h .. +7 of this lane's key
-        const int rg = (qw0 + 16 * hi + 8 * h) >> 2;
-        keep = drop_rows4(a.drop, key, rg, bhq) | (drop_rows4(a.drop, key, rg + 1, bhq) << 4);
-      }
+      const uint32_t keep = keep16 >> (8 * hi);
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
         const int i = 8 * hi + x;
@@ -576,15 +575,14 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[kb][i] = 32 * kb + (i & 7) + 16 * (i >> 3) >= thr ? kNegInf : s[kb][i];
     }
+    // dropout: keep bit 16kb + 8hi + x of key kv0 + 32kb + 16hi + 8h + x for row qi
+    uint32_t keep32 = 0xffffffffu;
+    if constexpr (DROP) keep32 = drop_tile_keys(a.drop, (kv0 + 8 * h) >> 2, qi, bh);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int hi = 0; hi < 2; ++hi) {
-        uint32_t keep = 0xff;
-        if constexpr (DROP) {  // keys kv0 + 32kb + 16hi + 8h .. +7 of row qi
-          const int kg = (kv0 + 32 * kb + 16 * hi + 8 * h) >> 2;
-          keep = drop_keys4(a.drop, kg, qi, bh) | (drop_keys4(a.drop, kg + 1, qi, bh) << 4);
-        }
+        const uint32_t keep = keep32 >> (16 * kb + 8 * hi);
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
           const int i = 8 * hi + x;

@@ -161,6 +161,53 @@ __device__ __forceinline__ uint32_t drop_keys4(const Dropout& dp, int kg, int ro
   const int r = row & 3;
   return drop_bits(dp, r == 0 ? w[0] : r == 1 ? w[1] : r == 2 ? w[2] : w[3]);
 }
+// Value of x in lane S of this lane's quad (DPP quad_perm broadcast).
+template <int S>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, S | (S << 2) | (S << 4) | (S << 6), 0xf, 0xf, false);
+}
+__device__ __forceinline__ uint32_t pick4(int r, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return r == 0 ? a : r == 1 ? b : r == 2 ? c : d;
+}
+
+// Keep bits of one lane's row for the 64 keys 4 kgb .. +63 of a tile laid out as the score
+// accumulators hold them (lane = query row; the four lanes of a quad are rows 4a .. 4a+3 of one
+// row group and see the same keys): bit 8m + 4g + x is key 4 (kgb + 4m + g) + x. The eight
+// Philox calls these 64 keys need are the same for the whole quad, so lane r computes calls r
+// and r + 4 and the quad shares the words through DPP broadcasts (row = 4a + r).
+__device__ __forceinline__ uint32_t drop_tile_keys(const Dropout& dp, int kgb, int row, int bh) {
+  const int a = row >> 2, r = row & 3;
+  const u32x4 wa = drop_block(dp, kgb + 4 * (r >> 1) + (r & 1), a, bh);      // call c = r
+  const u32x4 wb = drop_block(dp, kgb + 8 + 4 * (r >> 1) + (r & 1), a, bh);  // call c = r + 4
+  uint32_t keep = 0;
+#define FA_DROP_CALL(C, W, S)                                                                       \
+  keep |= drop_bits(dp, pick4(r, quad_bcast<S>(W[0]), quad_bcast<S>(W[1]), quad_bcast<S>(W[2]),     \
+                              quad_bcast<S>(W[3])))                                                 \
+          << (4 * (C));
+  FA_DROP_CALL(0, wa, 0) FA_DROP_CALL(1, wa, 1) FA_DROP_CALL(2, wa, 2) FA_DROP_CALL(3, wa, 3)
+  FA_DROP_CALL(4, wb, 0) FA_DROP_CALL(5, wb, 1) FA_DROP_CALL(6, wb, 2) FA_DROP_CALL(7, wb, 3)
+#undef FA_DROP_CALL
+  return keep;
+}
+
+// Keep bits of one lane's key for the 16 rows 4 rgb + 16 hi + 4 g + x (bit 8 hi + 4 g + x), the
+// layout of the dK/dV kernel's accumulators (lane = key; a quad's lanes are keys 4m .. 4m+3 and
+// see the same rows): the four calls are the same for the quad, lane r computes call r.
+__device__ __forceinline__ uint32_t drop_tile_rows(const Dropout& dp, int rgb, int key, int bh) {
+  const int r = key & 3, sh = 8 * r;
+  const u32x4 w = drop_block(dp, key >> 2, rgb + 4 * (r >> 1) + (r & 1), bh);  // call c = r
+  uint32_t keep = 0;
+#define FA_DROP_CALL(C)                                                                              \
+  keep |= ((((quad_bcast<C>(w[0]) >> sh) & 255u) >= dp.t ? 1u : 0u) |                                \
+           (((quad_bcast<C>(w[1]) >> sh) & 255u) >= dp.t ? 2u : 0u) |                                \
+           (((quad_bcast<C>(w[2]) >> sh) & 255u) >= dp.t ? 4u : 0u) |                                \
+           (((quad_bcast<C>(w[3]) >> sh) & 255u) >= dp.t ? 8u : 0u))                                 \
+          << (4 * (C));
+  FA_DROP_CALL(0) FA_DROP_CALL(1) FA_DROP_CALL(2) FA_DROP_CALL(3)
+#undef FA_DROP_CALL
+  return keep;
+}
+
 // keep mask (bit r) of the 4 rows 4 rg .. +3 for key `key`
 __device__ __forceinline__ uint32_t drop_rows4(const Dropout& dp, int key, int rg, int bh) {
   const u32x4 w = drop_block(dp, key >> 2, rg, bh);

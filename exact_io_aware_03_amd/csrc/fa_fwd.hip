@@ -319,6 +319,11 @@ __device__ __forceinline__ void tile_step(char* smem, int j, const char* kp, con
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[qh][kb][i] = fast_exp2(fmaf(s[qh][kb][i], c, -m_use[qh]));
   // ---- phase B: O^T += V^T P^T (MFMA) interleaved with packing and the row sums (VALU) ----
+  uint32_t keep[QH];  // dropout (§2.8): keep bit 8ks + x of key kv0 + 16ks + 8h + x, this lane's row
+  if constexpr (DROP) {
+#pragma unroll
+    for (int qh = 0; qh < QH; ++qh) keep[qh] = drop_tile_keys(dp, (kv0 + 8 * h) >> 2, q0 + 32 * qh + l32, bh);
+  }
 #pragma unroll
   for (int ks = 0; ks < BC / 16; ++ks) {
     bf16x8 pf[QH];
@@ -328,13 +333,12 @@ __device__ __forceinline__ void tile_step(char* smem, int j, const char* kp, con
       const int e = (ks & 1) * 8;
       u32x4 pw;
       if constexpr (DROP) {
-        // dropout on P (§2.8): this lane's 8 keys kv0 + 16ks + 8h .. +7 of row q0 + 32qh + l32;
-        // the row sum l keeps the undropped values
-        const int qi = q0 + 32 * qh + l32, kg = (kv0 + 16 * ks + 8 * h) >> 2;
-        const uint32_t keep = drop_keys4(dp, kg, qi, bh) | (drop_keys4(dp, kg + 1, qi, bh) << 4);
+        // dropout on P: this lane's 8 keys kv0 + 16ks + 8h .. +7; the row sum l keeps the
+        // undropped values
+        const uint32_t k8 = keep[qh] >> (8 * ks);
         float pd[8];
 #pragma unroll
-        for (int x = 0; x < 8; ++x) pd[x] = (keep >> x) & 1 ? sv[e + x] * dp.scale : 0.f;
+        for (int x = 0; x < 8; ++x) pd[x] = (k8 >> x) & 1 ? sv[e + x] * dp.scale : 0.f;
 #pragma unroll
         for (int x = 0; x < 4; ++x) pw[x] = pack_bf16x2(pd[2 * x], pd[2 * x + 1]);
       } else {
