@@ -306,6 +306,28 @@ def main():
         del q, k, v, q8, k8, qs, ks, o, lse, signs
         torch.cuda.empty_cache()
 
+        # dropout on P (p = 0.1) on the training shape without the mask: forward and backward
+        # regenerate the keep mask from (seed, offset); FLOPs counted as without dropout
+        log("[bench] dropout_b16h16n2048d128")
+        inp = workloads.make_attention_inputs(w.B, w.Nq, w.Nk, w.Hq, w.Hkv, w.d, w.seed, w.dtype, with_do=True)
+        q, k, v, do = dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["do"])
+        del inp
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda")
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.Hq, w.Nq, w.d), dtype=torch.uint8, device="cuda")
+        pd, seed = 0.1, 0x5EED
+        f_ms = float(np.mean(time_launches(
+            lambda: fa.fa_fwd_dropout(q, k, v, o, lse, pd, seed, 0, scale=w.scale), args.reps * 2, 3)))
+        b_ms = float(np.mean(time_launches(
+            lambda: fa.fa_bwd_dropout(q, k, v, o, do, lse, dq, dk, dv, ws, pd, seed, 0, scale=w.scale), args.reps, 2)))
+        for kind, ms, fl in (("fwd", f_ms, ff[False]), ("bwd", b_ms, bf[False])):
+            tf = fl / (ms * 1e-3) / 1e12
+            results[f"{kind}_dropout0.1_nc_b16h16n2048d128"] = {"ms": round(ms, 4), "tflops": round(tf, 2),
+                                                               "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        del q, k, v, do, o, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+
     line = {
         "metric": METRIC,
         "value": round(value, 2),

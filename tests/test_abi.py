@@ -172,3 +172,24 @@ def test_fp8_validation_and_scale_count():
     assert f(qs=None) == INVALID and f(ks=None) == INVALID and f(k8=None) == INVALID
     assert f(d=64) == UNSUPPORTED  # the FP8 forward is built for d = 128
     assert f(causal=1, Nk=9) == UNSUPPORTED and f(Hq=3, Hkv=2) == INVALID and f(scale=0.0) == INVALID
+
+
+def test_dropout_validation():
+    L = fa.lib()
+
+    def f(**kw):
+        a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=64, causal=0, scale=0.125, p=0.1,
+                 seed=1, off=0)
+        a.update(kw)
+        return L.fa_fwd_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"],
+                                a["d"], a["causal"], a["scale"], a["p"], a["seed"], a["off"], None)
+    assert f(p=1.0) == INVALID and f(p=-0.01) == INVALID and f(p=float("nan")) == INVALID
+    assert f(q=None) == INVALID and f(d=96) == UNSUPPORTED and f(causal=1, Nk=9) == UNSUPPORTED
+
+    def b(ws=P, ws_bytes=None, **kw):
+        a = dict(B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=64, causal=0, scale=0.125, p=0.1)
+        a.update(kw)
+        need = fa.fa_bwd_workspace_size(a["B"], a["Hq"], a["Nq"], a["d"])
+        return L.fa_bwd_dropout(P, P, P, P, P, P, P, P, P, a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"],
+                                a["causal"], a["scale"], a["p"], 5, 0, ws, need if ws_bytes is None else ws_bytes, None)
+    assert b(p=1.5) == INVALID and b(ws=None) == WORKSPACE and b(d=32) == UNSUPPORTED and b(Hq=3, Hkv=2) == INVALID
