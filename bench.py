@@ -220,7 +220,7 @@ def main():
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
     dom_call = "%s %s" % ("fa_fwd" if dom[0] == "fwd" else "fa_bwd", "causal" if dom[1] else "non-causal")
     dom_name = {"fwd": "fwd_bf16_kernel<128,%s>" % ("true" if dom[1] else "false"),
-                "bwd": "fa_bwd %s (bwd_pre + bwd_main_kernel<128> + bwd_dq_kernel<128>)" % ("causal" if dom[1] else "non-causal")}[dom[0]]
+                "bwd": "fa_bwd %s (bwd_dq_kernel<128> + bwd_main_kernel<128>)" % ("causal" if dom[1] else "non-causal")}[dom[0]]
     del q, k, v, do, o, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
 
@@ -261,7 +261,7 @@ def main():
         del q, k, v, o, lse, ws, lens
         torch.cuda.empty_cache()
 
-        # causal backward (pre + main + finalize), forward untimed
+        # causal backward (dQ kernel + dK/dV kernel), forward untimed
         w5 = workloads.WORKLOADS["bwd_bf16_causal_b8h16n4096d128"]
         log(f"[bench] {w5.name}")
         inp = workloads.make_workload_inputs(w5)

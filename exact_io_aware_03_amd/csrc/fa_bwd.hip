@@ -2,10 +2,11 @@
 //
 // Method (Lecture 21 notes, CMU 11-868, §2.6 and exercises 4-6): the forward keeps only O and
 // L = m + log l per row. The backward rebuilds each tile's P = exp(scale*S - L), forms
-// dV += P^T dO, dP = dO V^T, dS = P * (dP - D) with D = rowsum(dO * O) computed by a small
-// pre-kernel (sum_k P_ik dP_ik = dO_i . O_i), dK += scale dS^T Q and dQ += scale dS K.
+// dV += P^T dO, dP = dO V^T, dS = P * (dP - D) with D = rowsum(dO * O) (sum_k P_ik dP_ik =
+// dO_i . O_i), dK += scale dS^T Q and dQ += scale dS K.
 //
-// gfx950 mapping: two kernels after the pre-kernel, neither with atomics.
+// gfx950 mapping: two kernels, neither with atomics. The dQ kernel runs first and also writes
+// D for its rows (it loads O and dO for them anyway); the dK/dV kernel reads D afterwards.
 //  * dK/dV, key-block outer: a workgroup owns 128 keys of one (batch, kv head); its eight
 //    waves (two per SIMD) are four 32-key slices x two 32-row halves of every 64-row query
 //    block it walks (causal: only blocks at or below the diagonal, longest task first), for
@@ -27,7 +28,6 @@
 namespace fa {
 namespace {
 
-constexpr int kThreads = 256;             // pre / post kernels
 constexpr int kMainThreads = 512;         // main kernel: 8 waves, two per SIMD
 constexpr int kWaves = kMainThreads / 64;
 constexpr int BK = kBwdKeys;  // 128 keys per workgroup
@@ -176,31 +176,6 @@ __device__ __forceinline__ bf16x8 tr_frag(const char* base, int ks, int cb, int 
   typedef short i16x8 __attribute__((ext_vector_type(8)));
   const i16x8 c = __builtin_shufflevector(r[0], r[1], 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, c);
-}
-
-// D = rowsum(dO * O) per (batch, head, row): D/8 lanes per row, 16 bytes of O and dO each.
-template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a) {
-  constexpr int LPR = D / 8;  // lanes per row
-  const long row = ((long)blockIdx.x * kThreads + threadIdx.x) / LPR;  // (b*Nq + i)*Hq + h
-  const int sub = threadIdx.x % LPR;
-  const long rows = (long)a.B * a.Nq * a.Hq;
-  float s = 0.f;
-  if (row < rows) {
-    const u32x4 ow = *(const u32x4*)((const uint16_t*)a.o + row * D + sub * 8);
-    const u32x4 gw = *(const u32x4*)((const uint16_t*)a.dout + row * D + sub * 8);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      s = fmaf(bf16_lo(ow[e]), bf16_lo(gw[e]), s);
-      s = fmaf(bf16_hi(ow[e]), bf16_hi(gw[e]), s);
-    }
-  }
-#pragma unroll
-  for (int off = LPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-  if (row < rows && sub == 0) {
-    const int h = row % a.Hq, i = (row / a.Hq) % a.Nq, b = row / ((long)a.Hq * a.Nq);
-    a.dvec[((long)b * a.Hq + h) * a.Nq + i] = s;
-  }
 }
 
 // DROP: the forward's dropout on P (Lecture 21 notes §2.8, exercise 4), its mask regenerated:
@@ -478,20 +453,32 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   const int qi = q0 + l32;  // this lane's query row
   // Q and dO as B operands of S^T = K Q^T and dP^T = V dO^T: column qi, dims [16ks + 8h, +8)
   bf16x8 qf[KS], gf[KS];
+  // D = rowsum(dO * O) of row qi (§2.6), from this lane's half of the dims and its partner's;
+  // written for the dK/dV kernel, which runs after this one (rows past Nq read zeros)
+  float dd = 0.f;
   {
     const rsrc_t rq = make_rsrc((const uint16_t*)a.q + qbase, q_valid);
     const rsrc_t rg = make_rsrc((const uint16_t*)a.dout + qbase, q_valid);
+    const rsrc_t ro = make_rsrc((const uint16_t*)a.o + qbase, q_valid);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int off = (int)(((long)qi * a.q_row + ks * 16 + h * 8) * 2);
       qf[ks] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
-      gf[ks] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(rg, off, 0, 0));
+      const u32x4 gw = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, off, 0, 0));
+      const u32x4 ow = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0));
+      gf[ks] = as_bf16x8(gw);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dd = fmaf(bf16_lo(ow[e]), bf16_lo(gw[e]), dd);
+        dd = fmaf(bf16_hi(ow[e]), bf16_hi(gw[e]), dd);
+      }
     }
   }
-  float l2 = 0.f, dd = 0.f;  // L in base 2 and D of row qi (rows past Nq contribute nothing)
+  dd = halves_sum(dd);
+  float l2 = 0.f;  // L in base 2 of row qi (rows past Nq contribute nothing)
   if (qi < a.Nq) {
     l2 = a.lse[((long)b * a.Hq + hq) * a.Nq + qi] * kLog2e;
-    dd = a.dvec[((long)b * a.Hq + hq) * a.Nq + qi];
+    if (h == 0) a.dvec[((long)b * a.Hq + hq) * a.Nq + qi] = dd;
   }
 
   int n_tiles = (a.Nk + DQ_BC - 1) / DQ_BC;
@@ -630,18 +617,15 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dq_kernel(BwdArgs a) {
     }
 }
 
+// The dQ kernel runs first: besides dQ it computes D = rowsum(dO * O) for its rows (every row
+// belongs to exactly one of its workgroups) and stores it for the dK/dV kernel.
 template <int D, bool DROP>
 hipError_t launch_d(const BwdArgs& a, hipStream_t s) {
-  const long rows = (long)a.B * a.Nq * a.Hq, rows_per_block = kThreads / (D / 8);
-  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((rows + rows_per_block - 1) / rows_per_block), dim3(kThreads), 0, s,
-                     a);
+  if (a.causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true, DROP>), dim3(a.n_tasks_dq), dim3(kMainThreads), 0, s, a);
+  else hipLaunchKernelGGL((bwd_dq_kernel<D, false, DROP>), dim3(a.n_tasks_dq), dim3(kMainThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_main_kernel<D, DROP>), dim3(a.n_tasks), dim3(kMainThreads), 0, s, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (a.causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true, DROP>), dim3(a.n_tasks_dq), dim3(kMainThreads), 0, s, a);
-  else hipLaunchKernelGGL((bwd_dq_kernel<D, false, DROP>), dim3(a.n_tasks_dq), dim3(kMainThreads), 0, s, a);
   return hipGetLastError();
 }
 
