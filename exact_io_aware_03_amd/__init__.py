@@ -23,7 +23,7 @@ _STATUS = {0: "FA_OK", -1: "FA_ERR_INVALID_ARG", -2: "FA_ERR_UNSUPPORTED", -3: "
 EXPORTED = (
     "fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_workspace_size", "fa_strerror",
     "fa_version", "fa_wave_efficiency", "fa_plan_splits", "fa_schedule_makespan", "fa_causal_tiles",
-    "fa_decode_chunk", "fa_fp8_scale_count", "fa_quantize_fp8", "fa_fwd_fp8", "fa_fwd_dropout", "fa_bwd_dropout",
+    "fa_fp8_scale_count", "fa_quantize_fp8", "fa_fwd_fp8", "fa_fwd_dropout", "fa_bwd_dropout",
 )
 
 _lib = None
@@ -65,8 +65,6 @@ def lib() -> ctypes.CDLL:
     L.fa_schedule_makespan.restype = i
     L.fa_causal_tiles.argtypes = [i, i, i]
     L.fa_causal_tiles.restype = ctypes.c_long
-    L.fa_decode_chunk.argtypes = [i, i, i]
-    L.fa_decode_chunk.restype = i
     L.fa_fp8_scale_count.argtypes = [i, i, i]
     L.fa_fp8_scale_count.restype = sz
     L.fa_quantize_fp8.argtypes = [vp] * 4 + [i] * 4 + [vp]
@@ -297,5 +295,3 @@ def causal_tiles(n: int, br: int, bc: int) -> int:
     return int(lib().fa_causal_tiles(n, br, bc))
 
 
-def decode_chunk(B: int, Hkv: int, Nk_max: int) -> int:
-    return int(lib().fa_decode_chunk(B, Hkv, Nk_max))

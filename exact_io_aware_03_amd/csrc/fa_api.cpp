@@ -215,25 +215,10 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
                     ws_bytes, &dp, stream);
 }
 
-int fa_decode_chunk(int B, int Hkv, int Nk_max) {
-  if (B < 1 || Hkv < 1 || Nk_max < 1) return fa::kDecMinChunk;
-  if (const char* env = std::getenv("FA_DECODE_CHUNK")) {  // sweep override, multiple of 256
-    const int c = std::atoi(env);
-    if (c >= fa::kDecMinChunk && c % fa::kDecMinChunk == 0 && c <= 8192) return c;
-  }
-  // Largest chunk that still gives at least 8192 (sequence, kv head, chunk) units, i.e. a
-  // few dozen per CU even when lengths are ragged; longer chunks cut partial traffic.
-  for (int c : {2048, 1024, 512}) {
-    const long units = (long)B * Hkv * ((Nk_max + c - 1) / c);
-    if (units >= 8192) return c;
-  }
-  return fa::kDecMinChunk;
-}
-
 size_t fa_decode_workspace_size(int B, int Hq, int Nk_max, int d) {
   if (B < 1 || Hq < 1 || Nk_max < 1 || d < 1) return 0;
-  const size_t slots = (size_t)B * Hq * ((Nk_max + fa::kDecMinChunk - 1) / fa::kDecMinChunk);
-  return align256(slots * d * sizeof(float)) + slots * 2 * sizeof(float);
+  const size_t slots = (size_t)(fa::kDecMaxWorkers + B) * Hq;
+  return align256(slots * d * sizeof(float)) + align256(slots * 2 * sizeof(float)) + (size_t)(B + 1) * sizeof(int);
 }
 
 int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int* seqlens_k, void* o, float* lse,
@@ -252,11 +237,10 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int
   fa::DecArgs a{};
   a.q = q; a.k = k_cache; a.v = v_cache; a.seqlens = seqlens_k; a.o = o; a.lse = lse;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.Nk_max = Nk_max; a.d = d;
-  a.chunk = fa_decode_chunk(B, Hkv, Nk_max);
-  a.n_chunks_max = (Nk_max + fa::kDecMinChunk - 1) / fa::kDecMinChunk;
-  const size_t slots = (size_t)B * Hq * a.n_chunks_max;
+  const size_t slots = (size_t)(fa::kDecMaxWorkers + B) * Hq;
   a.part_o = (float*)workspace;
   a.part_ml = (float*)((char*)workspace + align256(slots * d * sizeof(float)));
+  a.pref = (int*)((char*)a.part_ml + align256(slots * 2 * sizeof(float)));
   a.k_row = (long)Hkv * d;
   a.c = scale * 1.4426950408889634f;
   return hip_status(fa::launch_decode(a, (hipStream_t)stream));

@@ -6,17 +6,24 @@
 // merge order give the same result up to rounding; §6.2 GQA packing: the query heads that
 // share a K/V head are stacked as rows of one tile so K/V are read once per group).
 //
-// gfx950 mapping: one workgroup = (sequence b, kv head, chunk of `chunk` keys); the grid
-// covers the padded maximum length and chunks past a sequence's length exit at once, so the
-// ragged lengths stay on the device. The four waves take the chunk's 64-key steps in turn and
-// stream them with whole-row 16-byte loads (the next step's loads in flight while this one
-// computes; K staged through LDS into MFMA operand order), compute S^T = K Q^T for the
-// packed query heads with v_mfma_f32_16x16x32_bf16 (query heads as the 16 MFMA columns), do
-// the online softmax on the VALU, and accumulate P V on the VALU with each lane owning D/16
-// head dims of one key in four. The four waves merge in LDS and write one fp32 partial per
-// (query head, chunk); the combine kernel merges the partials of each (sequence, query head).
-// The grid runs kv heads fastest, so the workgroups that share the cache rows of one key
-// range (the kv heads are interleaved within a row) are in flight together.
+// gfx950 mapping: a persistent grid, one workgroup per compute unit. The work is the list of
+// 64-key blocks of all sequences in order (sequence 0's blocks, then sequence 1's, ...); it is
+// cut into equal contiguous ranges, one per worker, so every worker streams the same number of
+// bytes however ragged the lengths are, and the lengths never leave the device. A worker is a
+// set of waves of one workgroup, one wave per kv head (several heads per wave when there are
+// more kv heads than waves; several workers per workgroup when there are fewer): since the
+// cache interleaves the kv heads within each key's row, the waves of a worker read whole
+// contiguous rows between them. Each wave walks its range one 64-key block at a time with
+// whole-row 16-byte loads, the next block's loads in flight while the current one computes
+// (the pipeline restarts at each new (sequence, kv head) job, one or two per wave here);
+// K is staged through LDS into MFMA operand order, S^T = K Q^T for the packed query heads comes
+// from v_mfma_f32_16x16x32_bf16 (query heads as the 16 MFMA columns), the online softmax and
+// the P V product run on the VALU (each lane owns D/16 head dims of one key in four). A wave
+// writes one fp32 partial (o, m, l) per (kv head, sequence it touched): a worker's ranges and
+// the sequences both advance monotonically through the block list, so (worker + sequence)
+// numbers the partials without collisions. The combine kernel merges the partials of each
+// (sequence, query head); the worker that holds a sequence's first block records where that
+// sequence starts in the list, which tells the combine which workers covered it.
 // Decode is bound by HBM: every cached K/V byte is read exactly once.
 #include "fa_device.h"
 #include "fa_internal.h"
@@ -24,8 +31,7 @@
 namespace fa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kStep = 64;  // keys per wave step
+constexpr int kUnit = 64;  // keys per block of the work list (one wave step)
 
 __device__ __forceinline__ float xor_max(float x) {
   x = fmaxf(x, __shfl_xor(x, 16));
@@ -35,57 +41,84 @@ __device__ __forceinline__ float xor_sum(float x) {
   x += __shfl_xor(x, 16);
   return x + __shfl_xor(x, 32);
 }
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+__device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+// Orders this wave's LDS accesses and keeps the compiler from moving them across the point.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
-// D: head dim (64 or 128). GM: query heads per kv head the registers are sized for.
-template <int D, int GM>
-__global__ __launch_bounds__(kThreads, GM <= 4 ? 2 : 1) void decode_partial_kernel(DecArgs a) {
+// Cached length of sequence b, clamped to [1, Nk_max], and its number of 64-key blocks.
+__device__ __forceinline__ int seq_len(const DecArgs& a, int b) { return min(max(a.seqlens[b], 1), a.Nk_max); }
+__device__ __forceinline__ int seq_blocks(int n) { return (n + kUnit - 1) / kUnit; }
+
+// D: head dim (64 or 128). GM: query heads per kv head the registers are sized for. NW: waves
+// per workgroup (8 when GM = 4; 4 for the larger groups, whose accumulators need a SIMD's
+// whole register file per wave).
+template <int D, int GM, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void decode_partial_kernel(DecArgs a) {
   constexpr int KS = D / 32;  // 32-dim MFMA steps
   constexpr int VE = D / 16;  // head dims per lane in the P V product
   constexpr int CH = D / 8;     // 16-byte chunks per K/V row
   constexpr int KPI = 64 / CH;  // keys per row-wise load instruction
-  __shared__ __attribute__((aligned(16))) char k_lds[4][kStep * D * 2];  // per-wave K staging
-  __shared__ float p_lds[4][kStep][GM];
-  __shared__ float alpha_lds[4][GM];
-  __shared__ float m_lds[4][GM], l_lds[4][GM];
-  // the cross-wave merge reuses the K staging area once every wave has left the key loop
-  static_assert(4 * GM * D * 4 <= sizeof(k_lds), "merge buffer");
-  float (*o_lds)[GM][D] = reinterpret_cast<float (*)[GM][D]>(&k_lds[0][0]);
+  constexpr int STAGE = kUnit * D * 2;
+  // Per-wave K staging. Once the scores have read K, the same bytes hold the block's
+  // probabilities p[key][head] and the rescale factors until the next block is staged.
+  __shared__ __attribute__((aligned(16))) char k_lds[NW][STAGE];
+  static_assert((kUnit * GM + GM) * 4 <= STAGE, "p overlay");
 
-  const int hk = blockIdx.x, chunk_id = blockIdx.y, b = blockIdx.z;
-  const int n = min(max(a.seqlens[b], 1), a.Nk_max);  // lengths outside [1, Nk_max] are clamped
-  const int k_begin = chunk_id * a.chunk;
-  if (k_begin >= n) return;  // past this sequence's length: nothing to read
-  const int k_end = min(n, k_begin + a.chunk);
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g4 = lane >> 4, l16 = lane & 15;
   const int G = a.G;
-  const int hq0 = hk * G;
+  // Waves side by side over kv heads; when there are fewer kv heads than waves, the workgroup
+  // holds S workers.
+  const int Hw = min(a.Hkv, NW), S = max(1, NW / a.Hkv);
+  const int hw = wave % Hw, sub = wave / Hw;
+  const int vw = (int)blockIdx.x * S + sub;  // worker index
 
-  const uint16_t* kp = (const uint16_t*)a.k + (long)b * a.Nk_max * a.k_row + hk * D;
-  const uint16_t* vp = (const uint16_t*)a.v + (long)b * a.Nk_max * a.k_row + hk * D;
+  // ---- this worker's range [u0, u1) of the block list (every wave derives it alone) ----
+  // Block indices fit in int: B * Nk_max * Hkv * 128 < 2^31 is checked on the host.
+  int U = 0;
+  for (int c0 = 0; c0 < a.B; c0 += 64) U += wave_sum(c0 + lane < a.B ? seq_blocks(seq_len(a, c0 + lane)) : 0);
+  U = __builtin_amdgcn_readfirstlane(U);
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.pref[a.B] = U;
+  if (sub >= S) return;  // spare wave (kv heads do not divide the waves evenly)
+  const int u0 = (int)((long)vw * U / a.n_workers), u1 = (int)((long)(vw + 1) * U / a.n_workers);
+  if (u0 >= u1) return;
 
-  // Q^T as the B operand: lane holds query head l16 (zero past G), dims [32ks + 8g4, +8).
-  bf16x8 qf[KS];
+  // First sequence whose blocks reach past u0, and where its blocks start.
+  int b = 0, pb = 0;
   {
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    const uint16_t* qp = (const uint16_t*)a.q + ((long)b * a.Hq + hq0 + l16) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf16x8(l16 < G ? *(const u32x4*)(qp + ks * 32 + g4 * 8) : zero);
+    int run = 0;
+    for (int c0 = 0; c0 < a.B; c0 += 64) {
+      const int nb = c0 + lane < a.B ? seq_blocks(seq_len(a, c0 + lane)) : 0;
+      const int inc = wave_inclusive_scan(nb, lane);
+      const unsigned long long hit = __ballot(c0 + lane < a.B && run + inc > u0);
+      if (hit) {
+        const int ln = __builtin_ctzll(hit);
+        b = c0 + ln;
+        pb = run + __shfl(inc - nb, ln);
+        break;
+      }
+      run += __shfl(inc, 63);
+    }
+    b = __builtin_amdgcn_readfirstlane(b);
+    pb = __builtin_amdgcn_readfirstlane(pb);
   }
-
-  float acc[GM][VE];
-#pragma unroll
-  for (int g = 0; g < GM; ++g)
-#pragma unroll
-    for (int e = 0; e < VE; ++e) acc[g][e] = 0.f;
-  float m = kNegInf, l = 0.f;
-
-  // The four waves take the chunk's 64-key steps in turn (wave w: steps w, w + 4, ...), so at
-  // any moment a workgroup reads one contiguous run of cache rows.
-  const int w_begin = k_begin + wave * kStep;
-  const int w_end = k_end;
-  constexpr int kStride = 4 * kStep;
 
   // K is read row-wise (CH lanes cover one key's row, KPI keys per instruction), which keeps
   // every request a whole row segment, and staged through this wave's LDS area, from where
@@ -93,191 +126,219 @@ __global__ __launch_bounds__(kThreads, GM <= 4 ? 2 : 1) void decode_partial_kern
   // chunks are XOR-swizzled by key so both the row-wise stores and the fragment reads are
   // free of bank conflicts. V rows stay in registers split over 16 lanes (lane l16 owns dims
   // [VE*l16, +VE) of keys 4s + g4). Loads go through a buffer resource that ends with the
-  // chunk's last key, so keys at or past w_end read as zeros without a memory access.
+  // job's last key, so keys at or past its end read as zeros without a memory access.
   u32x4 kr[CH];
   uint32_t vr[16][VE / 2];
-  // per-lane part of the offsets in a VGPR, the per-instruction row step in an SGPR
   const int koff = (int)(((lane / CH) * a.k_row + (lane % CH) * 8) * 2);
   const int voff = (int)((g4 * a.k_row + l16 * VE) * 2);
   const int row_b = (int)(a.k_row * 2);
   char* kl = k_lds[wave];
+  float* p_lds = reinterpret_cast<float*>(kl);  // [kUnit][GM] after the scores
+  float* alpha_lds = p_lds + kUnit * GM;        // [GM]
   auto kswz = [](int key) { return D == 128 ? (key & 15) : ((key >> 1) & 7); };
-  auto load_k = [&](int base) {
-    const rsrc_t r = make_rsrc(kp + (long)base * a.k_row, ((long)(w_end - 1 - base) * a.k_row + D) * 2);
-#pragma unroll
-    for (int i = 0; i < CH; ++i) kr[i] = __builtin_amdgcn_raw_buffer_load_b128(r, koff, i * KPI * row_b, 0);
-  };
-  auto stage_k = [&]() {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int key = i * KPI + lane / CH;
-      *(u32x4*)(kl + key * (D * 2) + (((lane % CH) ^ kswz(key)) << 4)) = kr[i];
-    }
-  };
-  auto load_v = [&](int base) {
-    const rsrc_t r = make_rsrc(vp + (long)base * a.k_row, ((long)(w_end - 1 - base) * a.k_row + D) * 2);
-#pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      if (VE == 8) {
-        const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 4 * s * row_b, 0);
-#pragma unroll
-        for (int e = 0; e < VE / 2; ++e) vr[s][e] = t[e];
-      } else {
-        const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 4 * s * row_b, 0);
-#pragma unroll
-        for (int e = 0; e < VE / 2; ++e) vr[s][e] = t[e];
-      }
-    }
-  };
 
-  // Software pipeline over 64-key steps: the next step's K is requested as soon as this
-  // step's scores have consumed K, the next V as soon as the P V product has consumed V, so
-  // each load has a whole step of arithmetic to arrive in.
-  load_k(w_begin);
-  load_v(w_begin);
-  for (int base = w_begin; base < w_end; base += kStride) {
-    stage_k();
-    load_k(base + kStride);
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // ---- scores: st[kb][r] is query head l16 against key base + 16kb + 4g4 + r ----
-    f32x4 st[4];
+  // Jobs: (sequence b, kv head hk) for each sequence the range touches and each head of the
+  // wave; a job's steps are the 64-key blocks [k_lo, k_hi) of b inside the range.
+  while (true) {
+    const int n = seq_len(a, b);
+    const int lo = max(u0, pb), hi = min(u1, pb + seq_blocks(n));
+    const int k_lo = (lo - pb) * kUnit, k_hi = min(n, (hi - pb) * kUnit);
+    // the worker holding a sequence's first block records where the sequence starts
+    if (lo == pb && hw == 0 && lane == 0) a.pref[b] = pb;
+    const long slot = (long)vw + b;
+    for (int hk = hw; hk < a.Hkv; hk += Hw) {
+      const uint16_t* kp = (const uint16_t*)a.k + (long)b * a.Nk_max * a.k_row + hk * D;
+      const uint16_t* vp = (const uint16_t*)a.v + (long)b * a.Nk_max * a.k_row + hk * D;
+      auto load_k = [&](int base) {
+        const rsrc_t r = make_rsrc(kp + (long)base * a.k_row, ((long)(k_hi - 1 - base) * a.k_row + D) * 2);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      st[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int key = kb * 16 + l16;
+        for (int i = 0; i < CH; ++i) kr[i] = __builtin_amdgcn_raw_buffer_load_b128(r, koff, i * KPI * row_b, 0);
+      };
+      auto stage_k = [&]() {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 f = *(const u32x4*)(kl + key * (D * 2) + (((4 * ks + g4) ^ kswz(key)) << 4));
-        st[kb] = mfma_16x16x32(as_bf16x8(f), qf[ks], st[kb]);
+        for (int i = 0; i < CH; ++i) {
+          const int key = i * KPI + lane / CH;
+          *(u32x4*)(kl + key * (D * 2) + (((lane % CH) ^ kswz(key)) << 4)) = kr[i];
+        }
+      };
+      auto load_v = [&](int base) {
+        const rsrc_t r = make_rsrc(vp + (long)base * a.k_row, ((long)(k_hi - 1 - base) * a.k_row + D) * 2);
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+          if (VE == 8) {
+            const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 4 * s * row_b, 0);
+#pragma unroll
+            for (int e = 0; e < VE / 2; ++e) vr[s][e] = t[e];
+          } else {
+            const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 4 * s * row_b, 0);
+#pragma unroll
+            for (int e = 0; e < VE / 2; ++e) vr[s][e] = t[e];
+          }
+        }
+      };
+      // Q^T as the B operand: lane holds query head l16 (zero past G), dims [32ks + 8g4, +8).
+      const int hq0 = hk * G;
+      bf16x8 qf[KS];
+      {
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        const uint16_t* qp = (const uint16_t*)a.q + ((long)b * a.Hq + hq0 + l16) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf16x8(l16 < G ? *(const u32x4*)(qp + ks * 32 + g4 * 8) : zero);
       }
-    }
-    float mx = kNegInf;
+      float acc[GM][VE];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+      for (int g = 0; g < GM; ++g)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (base + kb * 16 + g4 * 4 + r >= w_end) st[kb][r] = kNegInf;
-        mx = fmaxf(mx, st[kb][r]);
-      }
-    mx = xor_max(mx);  // all 64 keys of the step, per query head
-    const float m_new = fmaxf(m, mx * a.c);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = fast_exp2(m - m_use);
-    float rs = 0.f;
+        for (int e = 0; e < VE; ++e) acc[g][e] = 0.f;
+      float m = kNegInf, l = 0.f;
+
+      // Software pipeline over the job's blocks: the next block's K is requested as soon as
+      // this block's K sits in LDS, its V as soon as the P V product has consumed this V.
+      load_k(k_lo);
+      load_v(k_lo);
+      for (int base = k_lo; base < k_hi; base += kUnit) {
+        stage_k();
+        load_k(base + kUnit);
+        wave_sync();
+        // ---- scores: st[kb][r] is query head l16 against key base + 16kb + 4g4 + r ----
+        f32x4 st[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 4; ++kb) {
+          st[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          const int key = kb * 16 + l16;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = fast_exp2(fmaf(st[kb][r], a.c, -m_use));
-        rs += p;
-        if (l16 < GM) p_lds[wave][kb * 16 + g4 * 4 + r][l16] = p;
-      }
-    l = l * alpha + rs;
-    m = m_new;
-    if (g4 == 0 && l16 < GM) alpha_lds[wave][l16] = alpha;
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // ---- rescale and accumulate P V ----
+          for (int ks = 0; ks < KS; ++ks) {
+            const u32x4 f = *(const u32x4*)(kl + key * (D * 2) + (((4 * ks + g4) ^ kswz(key)) << 4));
+            st[kb] = mfma_16x16x32(as_bf16x8(f), qf[ks], st[kb]);
+          }
+        }
+        float mx = kNegInf;
 #pragma unroll
-    for (int g = 0; g < GM; ++g) {
-      const float al = alpha_lds[wave][g];
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int e = 0; e < VE; ++e) acc[g][e] *= al;
-    }
+          for (int r = 0; r < 4; ++r) {
+            if (base + kb * 16 + g4 * 4 + r >= k_hi) st[kb][r] = kNegInf;
+            mx = fmaxf(mx, st[kb][r]);
+          }
+        mx = xor_max(mx);  // all 64 keys of the block, per query head
+        const float m_new = fmaxf(m, mx * a.c);  // finite: the block's first key is valid
+        const float alpha = fast_exp2(m - m_new);
+        float rs = 0.f;
+        wave_sync();  // the K fragment reads are done before p overwrites the staging
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      float pv[GM];
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int g = 0; g < GM; ++g) pv[g] = p_lds[wave][4 * s + g4][g];
-#pragma unroll
-      for (int e = 0; e < VE / 2; ++e) {
-        const float v0 = bf16_lo(vr[s][e]), v1 = bf16_hi(vr[s][e]);
+          for (int r = 0; r < 4; ++r) {
+            const float p = fast_exp2(fmaf(st[kb][r], a.c, -m_new));
+            rs += p;
+            if (l16 < GM) p_lds[(kb * 16 + g4 * 4 + r) * GM + l16] = p;
+          }
+        l = l * alpha + rs;
+        m = m_new;
+        if (g4 == 0 && l16 < GM) alpha_lds[l16] = alpha;
+        wave_sync();
+        // ---- rescale and accumulate P V ----
 #pragma unroll
         for (int g = 0; g < GM; ++g) {
-          acc[g][2 * e] = fmaf(pv[g], v0, acc[g][2 * e]);
-          acc[g][2 * e + 1] = fmaf(pv[g], v1, acc[g][2 * e + 1]);
+          const float al = alpha_lds[g];
+#pragma unroll
+          for (int e = 0; e < VE; ++e) acc[g][e] *= al;
+        }
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+          float pv[GM];
+#pragma unroll
+          for (int g = 0; g < GM; ++g) pv[g] = p_lds[(4 * s + g4) * GM + g];
+#pragma unroll
+          for (int e = 0; e < VE / 2; ++e) {
+            const float v0 = bf16_lo(vr[s][e]), v1 = bf16_hi(vr[s][e]);
+#pragma unroll
+            for (int g = 0; g < GM; ++g) {
+              acc[g][2 * e] = fmaf(pv[g], v0, acc[g][2 * e]);
+              acc[g][2 * e + 1] = fmaf(pv[g], v1, acc[g][2 * e + 1]);
+            }
+          }
+        }
+        load_v(base + kUnit);
+        wave_sync();  // p and alpha are read before the next block is staged over them
+      }
+
+      // ---- the job's partial: merge the four key groups of the wave, write (o, m, l) ----
+      l = xor_sum(l);
+#pragma unroll
+      for (int g = 0; g < GM; ++g) {
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc[g][e] = xor_sum(acc[g][e]);
+        if (g4 == 0 && g < G) {
+          float* po = a.part_o + ((slot * a.Hq) + hq0 + g) * D + l16 * VE;
+#pragma unroll
+          for (int e = 0; e < VE; e += 4) *(f32x4*)(po + e) = f32x4{acc[g][e], acc[g][e + 1], acc[g][e + 2], acc[g][e + 3]};
         }
       }
+      if (g4 == 0 && l16 < G) {
+        float* pm = a.part_ml + ((slot * a.Hq) + hq0 + l16) * 2;
+        pm[0] = m;
+        pm[1] = l;
+      }
     }
-    load_v(base + kStride);
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  }
-
-  // ---- merge the four key groups of the wave, then the four waves ----
-  l = xor_sum(l);
-#pragma unroll
-  for (int g = 0; g < GM; ++g)
-#pragma unroll
-    for (int e = 0; e < VE; ++e) acc[g][e] = xor_sum(acc[g][e]);
-  __syncthreads();  // every wave is done with its K staging area, which now holds o_lds
-  if (g4 == 0) {
-    if (l16 < GM) {
-      m_lds[wave][l16] = m;
-      l_lds[wave][l16] = l;
-    }
-#pragma unroll
-    for (int g = 0; g < GM; ++g)
-#pragma unroll
-      for (int e = 0; e < VE; ++e) o_lds[wave][g][l16 * VE + e] = acc[g][e];
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-    const int g = idx / D, dd = idx % D;
-    float mm = kNegInf;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) mm = fmaxf(mm, m_lds[w][g]);
-    float ll = 0.f, oo = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float f = fast_exp2(m_lds[w][g] - mm);  // empty waves carry m = -inf -> f = 0
-      ll += f * l_lds[w][g];
-      oo += f * o_lds[w][g][dd];
-    }
-    const long slot = ((long)b * a.Hq + hq0 + g) * a.n_chunks_max + chunk_id;
-    a.part_o[slot * D + dd] = oo;
-    if (dd == 0) {
-      a.part_ml[slot * 2 + 0] = mm;
-      a.part_ml[slot * 2 + 1] = ll;
-    }
+    pb += seq_blocks(n);
+    if (++b >= a.B || pb >= u1) break;
   }
 }
 
 // Merge the partials of one (sequence, query head): O = sum_c 2^(m_c - M) o_c / l,
-// l = sum_c 2^(m_c - M) l_c, L = (M + log2 l) ln 2.
+// l = sum_c 2^(m_c - M) l_c, L = (M + log2 l) ln 2. The sequence's blocks are [P_b, P_b+1) of
+// the block list; worker w holds [w U / W, (w+1) U / W), so the last worker starting at or
+// before block u is floor(((u + 1) W - 1) / U). Workers in between with an empty range (more
+// workers than blocks) wrote nothing and are skipped.
 template <int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecArgs a) {
   const int b = blockIdx.x / a.Hq, hq = blockIdx.x % a.Hq;
-  const int n = min(max(a.seqlens[b], 1), a.Nk_max);
-  const int nc = (n + a.chunk - 1) / a.chunk;
-  const long slot0 = ((long)b * a.Hq + hq) * a.n_chunks_max;
+  const long p0 = a.pref[b], p1 = a.pref[b + 1], U = a.pref[a.B], W = a.n_workers;
+  const long w_lo = ((p0 + 1) * W - 1) / U, w_hi = (p1 * W - 1) / U;
+  auto holds_blocks = [&](long w) { return w * U / W < (w + 1) * U / W; };
   float mm = kNegInf;
-  for (int c = 0; c < nc; ++c) mm = fmaxf(mm, a.part_ml[(slot0 + c) * 2]);
+  for (long w = w_lo; w <= w_hi; ++w)
+    if (holds_blocks(w)) mm = fmaxf(mm, a.part_ml[((w + b) * a.Hq + hq) * 2]);
   float ll = 0.f, oo = 0.f;
   const int dd = threadIdx.x;
-  for (int c = 0; c < nc; ++c) {
-    const float f = fast_exp2(a.part_ml[(slot0 + c) * 2] - mm);
-    ll += f * a.part_ml[(slot0 + c) * 2 + 1];
-    oo += f * a.part_o[(slot0 + c) * D + dd];
+  for (long w = w_lo; w <= w_hi; ++w) {
+    if (!holds_blocks(w)) continue;
+    const long slot = (w + b) * a.Hq + hq;
+    const float f = fast_exp2(a.part_ml[slot * 2] - mm);
+    ll += f * a.part_ml[slot * 2 + 1];
+    oo += f * a.part_o[slot * D + dd];
   }
   ((__bf16*)a.o)[((long)b * a.Hq + hq) * D + dd] = (__bf16)(oo / ll);
   if (dd == 0) a.lse[(long)b * a.Hq + hq] = (mm + __log2f(ll)) * kLn2;
 }
 
-template <int D>
-hipError_t launch_d(const DecArgs& a, hipStream_t s) {
-  const dim3 grid(a.Hkv, (a.Nk_max + a.chunk - 1) / a.chunk, a.B), block(kThreads);
-  if (a.G <= 4) hipLaunchKernelGGL((decode_partial_kernel<D, 4>), grid, block, 0, s, a);
-  else if (a.G <= 8) hipLaunchKernelGGL((decode_partial_kernel<D, 8>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((decode_partial_kernel<D, 16>), grid, block, 0, s, a);
-  hipError_t e = hipGetLastError();
+template <int D, int GM, int NW>
+hipError_t launch_dg(DecArgs a, hipStream_t s) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int S = a.Hkv < NW ? NW / a.Hkv : 1;
+  const long blocks_max = (long)a.B * ((a.Nk_max + kUnit - 1) / kUnit);
+  // one workgroup per compute unit, fewer when the padded batch has fewer blocks
+  long wg = cus < 1 ? 1 : cus;
+  if (wg > kDecMaxWorkers / S) wg = kDecMaxWorkers / S;
+  if (wg > (blocks_max + S - 1) / S) wg = (blocks_max + S - 1) / S;
+  if (wg < 1) wg = 1;
+  a.n_workers = (int)(wg * S);
+  hipLaunchKernelGGL((decode_partial_kernel<D, GM, NW>), dim3((unsigned)wg), dim3(NW * 64), 0, s, a);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.Hq), dim3(D), 0, s, a);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const DecArgs& a, hipStream_t s) {
+  if (a.G <= 4) return launch_dg<D, 4, 8>(a, s);
+  if (a.G <= 8) return launch_dg<D, 8, 4>(a, s);
+  return launch_dg<D, 16, 4>(a, s);
 }
 
 }  // namespace

@@ -43,11 +43,11 @@ struct DecArgs {
   const int* seqlens;
   void* o;
   float* lse;
-  float* part_o;   // [B, Hq, n_chunks_max, d] unnormalised partial outputs
-  float* part_ml;  // [B, Hq, n_chunks_max, 2] partial (max, sum) in base-2 units
+  float* part_o;   // [kDecMaxWorkers + B, Hq, d] unnormalised partial outputs
+  float* part_ml;  // [kDecMaxWorkers + B, Hq, 2] partial (max, sum) in base-2 units
+  int* pref;       // [B + 1] first 64-key block of each sequence in the block list; [B] = total
   int B, Hq, Hkv, G, Nk_max, d;
-  int chunk;         // keys per workgroup
-  int n_chunks_max;  // ceil(Nk_max / 256): stride of the partial arrays
+  int n_workers;   // set by the launcher: workers sharing the block list
   long k_row;
   float c;
 };
@@ -80,7 +80,7 @@ constexpr int kFwdRows = 256;     // query rows per bf16 / fp8 forward workgroup
 constexpr int kFwdF32Rows = 128;  // query rows per fp32 forward workgroup (4 waves x 32)
 constexpr int kFwdKeys = 64;      // keys per forward K/V tile
 constexpr int kFwdF32Keys = 32;   // keys per tile in the fp32 forward
-constexpr int kDecMinChunk = 256; // smallest decode chunk (4 waves x 64 keys)
+constexpr int kDecMaxWorkers = 2048;  // decode workers (partials per sequence boundary)
 constexpr int kBwdKeys = 128;     // keys per dK/dV workgroup (4 key slices x 32)
 constexpr int kBwdRows = 64;      // query rows per dK/dV inner step
 constexpr int kBwdDqRows = 256;   // query rows per dQ workgroup (8 waves x 32)

@@ -94,16 +94,19 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
                    float scale, float p_drop, unsigned long long seed, unsigned int offset, void* workspace,
                    size_t ws_bytes, void* stream);
 
-/* Workspace bytes fa_decode needs: split-KV partials for up to ceil(Nk_max/256) splits. */
+/* Workspace bytes fa_decode needs: fp32 partials (o, m, l) for up to 2048 + B splits of every
+ * query head, and B + 1 ints recording where each sequence starts in the list of key blocks. */
 size_t fa_decode_workspace_size(int B, int Hq, int Nk_max, int d);
 
 /*
  * Decode: one query per sequence against a padded KV cache (Lecture 21 notes §6.1-6.2).
  * q [B,1,Hq,d]; k_cache, v_cache [B,Nk_max,Hkv,d]; seqlens_k int32 [B] on the device: sequence b
  * attends its first seqlens_k[b] cached keys (values are clamped to [1, Nk_max]; rows past the
- * length are never read). The keys are split into chunks, each chunk yields a partial (m, l, o)
- * for the H_q/H_kv query heads that share a kv head, and a second kernel merges the partials by
- * logsumexp. Nq must be 1; dtype FA_BF16; H_q/H_kv <= 16. o [B,1,Hq,d] bf16, lse fp32 [B,Hq].
+ * length are never read). The 64-key blocks of all sequences, in order, are cut into equal
+ * contiguous ranges, one per worker of a persistent grid; a worker's piece of a sequence yields a
+ * partial (m, l, o) for the H_q/H_kv query heads that share a kv head, and a second kernel merges
+ * each sequence's partials by logsumexp. Nq must be 1; dtype FA_BF16; H_q/H_kv <= 16.
+ * o [B,1,Hq,d] bf16, lse fp32 [B,Hq].
  */
 int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int* seqlens_k, void* o,
               float* lse, int B, int Hq, int Hkv, int Nq, int Nk_max, int d, float scale, int dtype,
@@ -158,9 +161,6 @@ int fa_schedule_makespan(const int* w, int n, int workers, int longest_first, in
 /* Number of (query block, key tile) pairs a causal pass computes for N_q = N_k = n with
  * br-row query blocks and bc-key tiles, whole tiles above the diagonal skipped (§2.5). */
 long fa_causal_tiles(int n, int br, int bc);
-
-/* Keys per decode chunk the library would use for this shape (a multiple of 256). */
-int fa_decode_chunk(int B, int Hkv, int Nk_max);
 
 #ifdef __cplusplus
 }

@@ -147,12 +147,16 @@ def test_causal_tile_count_pin():
     assert fa.causal_tiles(2048, 128, 64) == sum(2 * i + 2 for i in range(2048 // 128)) <= T * T
 
 
-def test_decode_chunk_plan():
-    assert fa.decode_chunk(64, 8, 8192) == 512
-    assert fa.decode_chunk(1, 8, 8192) == 256
-    for B, H, N in [(1, 1, 1), (3, 5, 77), (128, 8, 131072)]:
-        c = fa.decode_chunk(B, H, N)
-        assert c % 256 == 0 and 256 <= c <= 2048
+def test_decode_workspace_size():
+    # fp32 partials (o, then m and l) for 2048 + B splits of every query head, each array padded
+    # to 256 bytes, then B + 1 int32 sequence starts
+    def pad(x):
+        return (x + 255) // 256 * 256
+
+    for B, Hq, d in [(64, 32, 128), (1, 1, 64), (3, 5, 128)]:
+        slots = (2048 + B) * Hq
+        assert fa.lib().fa_decode_workspace_size(B, Hq, 8192, d) == pad(slots * d * 4) + pad(slots * 8) + (B + 1) * 4
+    assert fa.lib().fa_decode_workspace_size(0, 32, 8192, 128) == 0
 
 
 def test_fp8_validation_and_scale_count():

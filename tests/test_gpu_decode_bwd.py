@@ -24,7 +24,12 @@ def run_decode(inp, scale):
     fa = _fa()
     q, k, v = (to_dev(inp[n], "bf16") for n in ("q", "k", "v"))
     lens = torch.from_numpy(inp["seqlens"]).cuda()
-    o, lse = fa.decode(q, k, v, lens, scale=scale)
+    B, _, Hq, d = q.shape
+    # workspace bytes all 0xFF (NaN as fp32): a read of a partial the kernels never wrote shows
+    ws = torch.full((fa.fa_decode_workspace_size(B, Hq, k.shape[1], d),), 255, dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    fa.fa_decode(q, k, v, lens, o, lse, ws, scale)
     torch.cuda.synchronize()
     return to_np(o), to_np(lse)
 
@@ -37,6 +42,16 @@ def run_decode(inp, scale):
         (2, 8, 8, 600, 64, [600, 3]),
         (2, 16, 2, 700, 128, [513, 64]),   # 8 query heads per kv head
         (2, 16, 1, 300, 64, [300, 129]),   # 16 query heads per kv head
+        # the persistent split of the block list: more sequences than one wave scans at once,
+        # more workers than blocks (empty workers), one sequence over many workers, kv heads
+        # that leave spare waves (3), several kv heads per wave (16), several workers per
+        # workgroup (1 kv head), a one-key cache
+        (100, 8, 8, 200, 128, [int(x) for x in np.random.default_rng(7).integers(1, 201, size=100)]),
+        (1, 8, 8, 8192, 128, [8192]),
+        (2, 6, 3, 500, 128, [500, 77]),
+        (2, 32, 16, 300, 64, [300, 190]),
+        (3, 4, 1, 1000, 128, [1000, 1, 640]),
+        (1, 2, 2, 1, 64, [1]),
     ],
 )
 def test_decode_small(B, Hq, Hkv, Nk_max, d, lengths):
