@@ -218,7 +218,7 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
 size_t fa_decode_workspace_size(int B, int Hq, int Nk_max, int d) {
   if (B < 1 || Hq < 1 || Nk_max < 1 || d < 1) return 0;
   const size_t slots = (size_t)(fa::kDecMaxWorkers + B) * Hq;
-  return align256(slots * d * sizeof(float)) + align256(slots * 2 * sizeof(float)) + (size_t)(B + 1) * sizeof(int);
+  return align256(slots * d * sizeof(float)) + align256(slots * 2 * sizeof(float)) + (size_t)B * 2 * sizeof(int);
 }
 
 int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int* seqlens_k, void* o, float* lse,
@@ -240,7 +240,7 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int
   const size_t slots = (size_t)(fa::kDecMaxWorkers + B) * Hq;
   a.part_o = (float*)workspace;
   a.part_ml = (float*)((char*)workspace + align256(slots * d * sizeof(float)));
-  a.pref = (int*)((char*)a.part_ml + align256(slots * 2 * sizeof(float)));
+  a.seq_w = (int*)((char*)a.part_ml + align256(slots * 2 * sizeof(float)));
   a.k_row = (long)Hkv * d;
   a.c = scale * 1.4426950408889634f;
   return hip_status(fa::launch_decode(a, (hipStream_t)stream));

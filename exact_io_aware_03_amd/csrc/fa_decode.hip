@@ -13,17 +13,16 @@
 // set of waves of one workgroup, one wave per kv head (several heads per wave when there are
 // more kv heads than waves; several workers per workgroup when there are fewer): since the
 // cache interleaves the kv heads within each key's row, the waves of a worker read whole
-// contiguous rows between them. Each wave walks its range one 64-key block at a time with
-// whole-row 16-byte loads, the next block's loads in flight while the current one computes
-// (the pipeline restarts at each new (sequence, kv head) job, one or two per wave here);
+// contiguous rows between them, in step with each other when the kv heads split evenly over the
+// waves. Each wave walks its range one 64-key block at a time with whole-row 16-byte loads;
 // K is staged through LDS into MFMA operand order, S^T = K Q^T for the packed query heads comes
 // from v_mfma_f32_16x16x32_bf16 (query heads as the 16 MFMA columns), the online softmax and
 // the P V product run on the VALU (each lane owns D/16 head dims of one key in four). A wave
 // writes one fp32 partial (o, m, l) per (kv head, sequence it touched): a worker's ranges and
 // the sequences both advance monotonically through the block list, so (worker + sequence)
-// numbers the partials without collisions. The combine kernel merges the partials of each
-// (sequence, query head); the worker that holds a sequence's first block records where that
-// sequence starts in the list, which tells the combine which workers covered it.
+// numbers the partials without collisions. The workers that hold a sequence's first and last
+// blocks record themselves, and the combine kernel merges the partials of the workers in
+// between for each (sequence, query head).
 // Decode is bound by HBM: every cached K/V byte is read exactly once.
 #include "fa_device.h"
 #include "fa_internal.h"
@@ -95,10 +94,15 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_partial_kernel(DecArgs a) {
   int U = 0;
   for (int c0 = 0; c0 < a.B; c0 += 64) U += wave_sum(c0 + lane < a.B ? seq_blocks(seq_len(a, c0 + lane)) : 0);
   U = __builtin_amdgcn_readfirstlane(U);
-  if (blockIdx.x == 0 && threadIdx.x == 0) a.pref[a.B] = U;
   if (sub >= S) return;  // spare wave (kv heads do not divide the waves evenly)
-  const int u0 = (int)((long)vw * U / a.n_workers), u1 = (int)((long)(vw + 1) * U / a.n_workers);
-  if (u0 >= u1) return;
+  // never more workers than blocks, so every worker's range is non-empty
+  const int W = min(a.n_workers, U);
+  if (vw >= W) return;
+  const int u0 = (int)((long)vw * U / W), u1 = (int)((long)(vw + 1) * U / W);
+  // When the kv heads split evenly over the waves, all waves of the workgroup run the same
+  // jobs and blocks; a barrier per block then keeps them reading the same cache rows at the
+  // same time (measured 2% faster than letting them drift apart).
+  const bool lockstep = a.Hkv % NW == 0;
 
   // First sequence whose blocks reach past u0, and where its blocks start.
   int b = 0, pb = 0;
@@ -143,8 +147,11 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_partial_kernel(DecArgs a) {
     const int n = seq_len(a, b);
     const int lo = max(u0, pb), hi = min(u1, pb + seq_blocks(n));
     const int k_lo = (lo - pb) * kUnit, k_hi = min(n, (hi - pb) * kUnit);
-    // the worker holding a sequence's first block records where the sequence starts
-    if (lo == pb && hw == 0 && lane == 0) a.pref[b] = pb;
+    // the workers holding a sequence's first and last blocks record themselves
+    if (hw == 0 && lane == 0) {
+      if (lo == pb) a.seq_w[2 * b] = vw;
+      if (hi == pb + seq_blocks(n)) a.seq_w[2 * b + 1] = vw;
+    }
     const long slot = (long)vw + b;
     for (int hk = hw; hk < a.Hkv; hk += Hw) {
       const uint16_t* kp = (const uint16_t*)a.k + (long)b * a.Nk_max * a.k_row + hk * D;
@@ -192,13 +199,14 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_partial_kernel(DecArgs a) {
         for (int e = 0; e < VE; ++e) acc[g][e] = 0.f;
       float m = kNegInf, l = 0.f;
 
-      // Software pipeline over the job's blocks: the next block's K is requested as soon as
-      // this block's K sits in LDS, its V as soon as the P V product has consumed this V.
-      load_k(k_lo);
-      load_v(k_lo);
+      // One block at a time: its K and V are requested together and the wave waits for them.
+      // Requesting the next block's K and V ahead (a software pipeline) was measured slower:
+      // more bytes in flight per wave read the cache rows in a less orderly way.
       for (int base = k_lo; base < k_hi; base += kUnit) {
+        if (lockstep) __syncthreads();
+        load_k(base);
+        load_v(base);
         stage_k();
-        load_k(base + kUnit);
         wave_sync();
         // ---- scores: st[kb][r] is query head l16 against key base + 16kb + 4g4 + r ----
         f32x4 st[4];
@@ -259,7 +267,6 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_partial_kernel(DecArgs a) {
             }
           }
         }
-        load_v(base + kUnit);
         wave_sync();  // p and alpha are read before the next block is staged over them
       }
 
@@ -286,28 +293,23 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_partial_kernel(DecArgs a) {
   }
 }
 
-// Merge the partials of one (sequence, query head): O = sum_c 2^(m_c - M) o_c / l,
-// l = sum_c 2^(m_c - M) l_c, L = (M + log2 l) ln 2. The sequence's blocks are [P_b, P_b+1) of
-// the block list; worker w holds [w U / W, (w+1) U / W), so the last worker starting at or
-// before block u is floor(((u + 1) W - 1) / U). Workers in between with an empty range (more
-// workers than blocks) wrote nothing and are skipped.
+// Merge the partials of one (sequence, query head), written by the workers first..last that
+// covered the sequence into slots (worker + sequence): O = sum_c 2^(m_c - M) o_c / l,
+// l = sum_c 2^(m_c - M) l_c, L = (M + log2 l) ln 2, with M the running maximum.
 template <int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecArgs a) {
   const int b = blockIdx.x / a.Hq, hq = blockIdx.x % a.Hq;
-  const long p0 = a.pref[b], p1 = a.pref[b + 1], U = a.pref[a.B], W = a.n_workers;
-  const long w_lo = ((p0 + 1) * W - 1) / U, w_hi = (p1 * W - 1) / U;
-  auto holds_blocks = [&](long w) { return w * U / W < (w + 1) * U / W; };
-  float mm = kNegInf;
-  for (long w = w_lo; w <= w_hi; ++w)
-    if (holds_blocks(w)) mm = fmaxf(mm, a.part_ml[((w + b) * a.Hq + hq) * 2]);
-  float ll = 0.f, oo = 0.f;
+  const int w_first = a.seq_w[2 * b], w_last = a.seq_w[2 * b + 1];
   const int dd = threadIdx.x;
-  for (long w = w_lo; w <= w_hi; ++w) {
-    if (!holds_blocks(w)) continue;
-    const long slot = (w + b) * a.Hq + hq;
-    const float f = fast_exp2(a.part_ml[slot * 2] - mm);
-    ll += f * a.part_ml[slot * 2 + 1];
-    oo += f * a.part_o[slot * D + dd];
+  float mm = kNegInf, ll = 0.f, oo = 0.f;
+  for (int w = w_first; w <= w_last; ++w) {
+    const long slot = ((long)w + b) * a.Hq + hq;
+    const float mc = a.part_ml[slot * 2], lc = a.part_ml[slot * 2 + 1], oc = a.part_o[slot * D + dd];
+    const float mn = fmaxf(mm, mc);
+    const float f_old = fast_exp2(mm - mn), f_new = fast_exp2(mc - mn);  // mm = -inf at first: 0
+    ll = ll * f_old + lc * f_new;
+    oo = oo * f_old + oc * f_new;
+    mm = mn;
   }
   ((__bf16*)a.o)[((long)b * a.Hq + hq) * D + dd] = (__bf16)(oo / ll);
   if (dd == 0) a.lse[(long)b * a.Hq + hq] = (mm + __log2f(ll)) * kLn2;

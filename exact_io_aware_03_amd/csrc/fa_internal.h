@@ -45,7 +45,7 @@ struct DecArgs {
   float* lse;
   float* part_o;   // [kDecMaxWorkers + B, Hq, d] unnormalised partial outputs
   float* part_ml;  // [kDecMaxWorkers + B, Hq, 2] partial (max, sum) in base-2 units
-  int* pref;       // [B + 1] first 64-key block of each sequence in the block list; [B] = total
+  int* seq_w;      // [B, 2] first and last worker that covered each sequence
   int B, Hq, Hkv, G, Nk_max, d;
   int n_workers;   // set by the launcher: workers sharing the block list
   long k_row;

@@ -95,7 +95,7 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
                    size_t ws_bytes, void* stream);
 
 /* Workspace bytes fa_decode needs: fp32 partials (o, m, l) for up to 2048 + B splits of every
- * query head, and B + 1 ints recording where each sequence starts in the list of key blocks. */
+ * query head, and two ints per sequence naming the first and last split that covered it. */
 size_t fa_decode_workspace_size(int B, int Hq, int Nk_max, int d);
 
 /*

@@ -149,13 +149,13 @@ def test_causal_tile_count_pin():
 
 def test_decode_workspace_size():
     # fp32 partials (o, then m and l) for 2048 + B splits of every query head, each array padded
-    # to 256 bytes, then B + 1 int32 sequence starts
+    # to 256 bytes, then the first and last worker of each sequence (int32)
     def pad(x):
         return (x + 255) // 256 * 256
 
     for B, Hq, d in [(64, 32, 128), (1, 1, 64), (3, 5, 128)]:
         slots = (2048 + B) * Hq
-        assert fa.lib().fa_decode_workspace_size(B, Hq, 8192, d) == pad(slots * d * 4) + pad(slots * 8) + (B + 1) * 4
+        assert fa.lib().fa_decode_workspace_size(B, Hq, 8192, d) == pad(slots * d * 4) + pad(slots * 8) + B * 8
     assert fa.lib().fa_decode_workspace_size(0, 32, 8192, 128) == 0
 
 

@@ -52,6 +52,10 @@ def run_decode(inp, scale):
         (2, 32, 16, 300, 64, [300, 190]),
         (3, 4, 1, 1000, 128, [1000, 1, 640]),
         (1, 2, 2, 1, 64, [1]),
+        # workgroups whose waves step through the blocks together: 8 query heads per kv head
+        # (4 waves, 2 kv heads each), 16 per kv head (4 waves, one kv head each)
+        (2, 64, 8, 400, 128, [400, 130]),
+        (2, 64, 4, 300, 64, [300, 65]),
     ],
 )
 def test_decode_small(B, Hq, Hkv, Nk_max, d, lengths):
