@@ -91,8 +91,12 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_partial_kernel(DecArgs a) {
 
   // ---- this worker's range [u0, u1) of the block list (every wave derives it alone) ----
   // Block indices fit in int: B * Nk_max * Hkv * 128 < 2^31 is checked on the host.
-  int U = 0;
-  for (int c0 = 0; c0 < a.B; c0 += 64) U += wave_sum(c0 + lane < a.B ? seq_blocks(seq_len(a, c0 + lane)) : 0);
+  // The first 64 sequences' block counts and their scan serve both passes (one pass over the
+  // lengths when B <= 64).
+  const int nb0 = lane < a.B ? seq_blocks(seq_len(a, lane)) : 0;
+  const int inc0 = wave_inclusive_scan(nb0, lane);
+  int U = __shfl(inc0, 63);
+  for (int c0 = 64; c0 < a.B; c0 += 64) U += wave_sum(c0 + lane < a.B ? seq_blocks(seq_len(a, c0 + lane)) : 0);
   U = __builtin_amdgcn_readfirstlane(U);
   if (sub >= S) return;  // spare wave (kv heads do not divide the waves evenly)
   // never more workers than blocks, so every worker's range is non-empty
@@ -109,8 +113,8 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_partial_kernel(DecArgs a) {
   {
     int run = 0;
     for (int c0 = 0; c0 < a.B; c0 += 64) {
-      const int nb = c0 + lane < a.B ? seq_blocks(seq_len(a, c0 + lane)) : 0;
-      const int inc = wave_inclusive_scan(nb, lane);
+      const int nb = c0 == 0 ? nb0 : (c0 + lane < a.B ? seq_blocks(seq_len(a, c0 + lane)) : 0);
+      const int inc = c0 == 0 ? inc0 : wave_inclusive_scan(nb, lane);
       const unsigned long long hit = __ballot(c0 + lane < a.B && run + inc > u0);
       if (hit) {
         const int ln = __builtin_ctzll(hit);
@@ -302,14 +306,25 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecArgs a) {
   const int w_first = a.seq_w[2 * b], w_last = a.seq_w[2 * b + 1];
   const int dd = threadIdx.x;
   float mm = kNegInf, ll = 0.f, oo = 0.f;
-  for (int w = w_first; w <= w_last; ++w) {
-    const long slot = ((long)w + b) * a.Hq + hq;
-    const float mc = a.part_ml[slot * 2], lc = a.part_ml[slot * 2 + 1], oc = a.part_o[slot * D + dd];
-    const float mn = fmaxf(mm, mc);
-    const float f_old = fast_exp2(mm - mn), f_new = fast_exp2(mc - mn);  // mm = -inf at first: 0
-    ll = ll * f_old + lc * f_new;
-    oo = oo * f_old + oc * f_new;
-    mm = mn;
+  // four partials' loads in flight at a time (indices past w_last re-read w_last, unused)
+  for (int w0 = w_first; w0 <= w_last; w0 += 4) {
+    float mc[4], lc[4], oc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const long slot = ((long)min(w0 + i, w_last) + b) * a.Hq + hq;
+      mc[i] = a.part_ml[slot * 2];
+      lc[i] = a.part_ml[slot * 2 + 1];
+      oc[i] = a.part_o[slot * D + dd];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (w0 + i > w_last) break;
+      const float mn = fmaxf(mm, mc[i]);
+      const float f_old = fast_exp2(mm - mn), f_new = fast_exp2(mc[i] - mn);  // mm = -inf at first: 0
+      ll = ll * f_old + lc[i] * f_new;
+      oo = oo * f_old + oc[i] * f_new;
+      mm = mn;
+    }
   }
   ((__bf16*)a.o)[((long)b * a.Hq + hq) * D + dd] = (__bf16)(oo / ll);
   if (dd == 0) a.lse[(long)b * a.Hq + hq] = (mm + __log2f(ll)) * kLn2;
