@@ -375,19 +375,48 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(BwdArgs a) {
   }
   wait_vm_barrier<0>();
   if (qhalf == 0) {
+    // Sum the halves in registers (every read of this slice's area comes before it is
+    // rewritten below; LDS accesses of one wave are ordered).
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int kk = kw0 + 8 * (i >> 2) + 4 * h + (i & 3);
-        const float dkv = dk[db][i] + red[((2 * db) * 16 + i) * 64];
-        const float dvv = dv[db][i] + red[((2 * db + 1) * 16 + i) * 64];
-        if (kk < a.Nk) {
-          const long off = ((long)b * a.Nk + kk) * a.k_row + hk * D + 32 * db + l32;
-          ((__bf16*)a.dk)[off] = (__bf16)(dkv * a.scale);
-          ((__bf16*)a.dv)[off] = (__bf16)dvv;
-        }
+        dk[db][i] = (dk[db][i] + red[((2 * db) * 16 + i) * 64]) * a.scale;
+        dv[db][i] += red[((2 * db + 1) * 16 + i) * 64];
       }
+    // Row-major bf16 tiles [32 keys][D] of dK and dV in this slice's area. Registers i, i+1
+    // (i even) hold keys r, r+1 for dim 32db + l32; adjacent lanes swap one value so the even
+    // lane packs dims (2m, 2m+1) of key r and the odd lane those of key r+1.
+    constexpr int ROWB = D * 2;
+    static_assert(2 * 32 * ROWB <= 2 * DB * 16 * 64 * 4, "bf16 tiles");
+    char* tile = reinterpret_cast<char*>((float*)smem + (size_t)slice * (2 * DB * 16 * 64));
+    const bool odd = lane & 1;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const int row = 8 * (i >> 2) + 4 * h + (i & 3) + (odd ? 1 : 0);
+        const int col = (32 * db + (l32 & ~1)) * 2;
+        const float sk = __shfl_xor(odd ? dk[db][i] : dk[db][i + 1], 1);
+        const float sv = __shfl_xor(odd ? dv[db][i] : dv[db][i + 1], 1);
+        *(uint32_t*)(tile + row * ROWB + col) = odd ? pack_bf16x2(sk, dk[db][i + 1]) : pack_bf16x2(dk[db][i], sk);
+        *(uint32_t*)(tile + 32 * ROWB + row * ROWB + col) =
+            odd ? pack_bf16x2(sv, dv[db][i + 1]) : pack_bf16x2(dv[db][i], sv);
+      }
+    // 16-byte stores of whole row segments; rows past the end of the keys are dropped by the
+    // buffer range.
+    const long base = ((long)b * a.Nk + kw0) * a.k_row + hk * D;
+    const long valid = kw0 < a.Nk ? ((long)(a.Nk - 1 - kw0) * a.k_row + D) * 2 : 0;
+    const rsrc_t rdk = make_rsrc((uint16_t*)a.dk + base, valid);
+    const rsrc_t rdv = make_rsrc((uint16_t*)a.dv + base, valid);
+    constexpr int CPR = ROWB / 16;  // 16-byte chunks per row
+#pragma unroll
+    for (int it = 0; it < 32 * CPR / 64; ++it) {
+      const int c = it * 64 + lane, row = c / CPR, ch = c % CPR;
+      const int goff = (int)(((long)row * a.k_row) * 2) + ch * 16;
+      __builtin_amdgcn_raw_buffer_store_b128(*(const u32x4*)(tile + row * ROWB + ch * 16), rdk, goff, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(*(const u32x4*)(tile + 32 * ROWB + row * ROWB + ch * 16), rdv, goff, 0, 0);
+    }
   }
 }
 
