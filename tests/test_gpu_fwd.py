@@ -94,6 +94,24 @@ def test_large_scores_no_overflow():
     assert np.abs(lse - rl).max() <= 1e-3 * max(1.0, np.abs(rl).max() / 64)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_rising_scores_move_the_reference(causal):
+    # scores rising by ~60 (base 2) along the keys: the conditional rescale (threshold 8) fires
+    # several times per row, in the masked diagonal tiles too
+    rng = np.random.Generator(np.random.PCG64(86))
+    B, N, H, d = 1, 1024, 2, 128
+    q = rng.standard_normal((B, N, H, d))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    ramp = np.linspace(0.0, 60.0 * math.log(2.0), N)
+    k = ramp[None, :, None, None] * q[:, :1] + 0.05 * rng.standard_normal((B, N, H, d))
+    v = rng.standard_normal((B, N, H, d))
+    inp = {n: workloads.round_to_bf16(x.astype(np.float32)) for n, x in (("q", q), ("k", k), ("v", v))}
+    o, lse = run_fwd(inp, causal, 1.0, "bf16")
+    ro, rl = ora.forward(inp["q"], inp["k"], inp["v"], causal, 1.0)
+    check("O", o, ro, "bf16")
+    check("L", lse, rl, "bf16", is_lse=True)
+
+
 def _sampled_config(w, causal, n_heads, n_rows, seed):
     say(f"fwd config {w.name} causal={causal}")
     inp = workloads.make_workload_inputs(w)

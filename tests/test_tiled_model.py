@@ -96,3 +96,47 @@ def test_causal_tile_count_pin():
     full = 4 * 1024 * 1024 * 64 / 1e6
     assert round(full, 1) == flop["full"]
     assert round(full * computed / (T * T), 1) == flop["skipped"]
+
+
+def _rising_scores(n, d, top, seed):
+    """q and keys whose scores rise linearly from 0 to `top` (base-2 units at scale 1) along
+    the keys, plus N(0,1) values."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = rng.standard_normal(d)
+    q /= np.linalg.norm(q)
+    ramp = np.linspace(0.0, top * math.log(2.0), n)
+    k = ramp[:, None] * q[None, :] + 0.05 * rng.standard_normal((n, d))
+    v = rng.standard_normal((n, d))
+    return q[None, :], k, v
+
+
+def test_conditional_rescaling_tau8_first_tile_only():
+    # Lecture 21 notes §5.3: with tau = 8 on N(0,1) data only the first tile sets the reference
+    # and the result is unchanged (the reference cancels in acc / l and m + log l)
+    rng = np.random.Generator(np.random.PCG64(83))
+    q, k, v = (rng.standard_normal((2048, 64)) for _ in range(3))
+    scale = 1.0 / math.sqrt(64)
+    o, lse, moves = tm.fwd_tiled_lazy(q, k, v, scale, tau=8.0)
+    ro, rl = ora.forward(q[None, :, None], k[None, :, None], v[None, :, None], False, scale)
+    assert np.all(moves == 1)
+    assert np.abs(o - ro[0, :, 0]).max() < 2e-5 and np.abs(lse - rl[0, 0]).max() < 1e-5
+
+
+def test_conditional_rescaling_moves_when_max_jumps():
+    # scores rising by 60 (base 2) along the row: the reference moves several times, each time
+    # by more than tau, and the result still equals the definition
+    q, k, v = _rising_scores(2048, 64, top=60.0, seed=84)
+    o, lse, moves = tm.fwd_tiled_lazy(q, k, v, 1.0, tau=8.0)
+    ro, rl = ora.forward(q[None, :, None], k[None, :, None], v[None, :, None], False, 1.0)
+    assert 2 <= moves[0] <= 60 // 8 + 1
+    assert np.abs(o - ro[0, :, 0]).max() < 1e-4 and abs(lse[0] - rl[0, 0, 0]) < 1e-4 * abs(rl[0, 0, 0])
+
+
+def test_conditional_rescaling_tau200_overflows_fp32():
+    # with tau = 200 a row whose scores grow by more than 128 (base 2) after its first tile
+    # pushes 2^(s - m) past the fp32 range: inf / NaN, the failure the notes report for tau = 200
+    q, k, v = _rising_scores(2048, 64, top=150.0, seed=85)
+    o, _, moves = tm.fwd_tiled_lazy(q, k, v, 1.0, tau=200.0)
+    assert moves[0] == 1 and not np.all(np.isfinite(o))
+    o8, _, _ = tm.fwd_tiled_lazy(q, k, v, 1.0, tau=8.0)
+    assert np.all(np.isfinite(o8))

@@ -55,6 +55,39 @@ def fwd_tiled(qh, kh, vh, scale, causal, br=128, bc=64, order=None):
     return o, lse
 
 
+def fwd_tiled_lazy(qh, kh, vh, scale, tau, bc=128):
+    """Non-causal online softmax in fp32 with conditional rescaling (Lecture 21 notes §5.3):
+    the reference max m of a row moves only when a tile's max exceeds it by more than tau
+    (base-2 units), so P = 2^(s - m) may reach 2^tau; acc and l are rescaled only then.
+
+    Returns (O, L, rescales) with rescales the number of reference moves per row (the first
+    tile's counts as one)."""
+    f32 = np.float32
+    q, k, v = (np.asarray(t, dtype=f32) for t in (qh, kh, vh))
+    nq, nk = q.shape[0], k.shape[0]
+    c = f32(scale / math.log(2.0))
+    m = np.full(nq, -np.inf, dtype=f32)
+    l = np.zeros(nq, dtype=f32)
+    acc = np.zeros((nq, v.shape[1]), dtype=f32)
+    moves = np.zeros(nq, dtype=np.int64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        for j0 in range(0, nk, bc):
+            j1 = min(nk, j0 + bc)
+            s = (q @ k[j0:j1].T) * c
+            tmax = s.max(axis=1)
+            move = tmax > m + f32(tau)
+            mn = np.where(move, tmax, m).astype(f32)
+            alpha = np.exp2(m - mn).astype(f32)  # 1 where the reference stays, 0 at the first tile
+            p = np.exp2(s - mn[:, None]).astype(f32)
+            l = (alpha * l + p.sum(axis=1, dtype=f32)).astype(f32)
+            acc = (alpha[:, None] * acc + p @ v[j0:j1]).astype(f32)
+            moves += move
+            m = mn
+        o = acc / l[:, None]
+        lse = (m.astype(np.float64) + np.log2(l.astype(np.float64))) * math.log(2.0)
+    return o, lse, moves
+
+
 def decode_partials(q, kh, vh, n, scale, chunk):
     """Split-KV partials (m2, l, o) for one sequence and one kv head; q is [G, d]."""
     c = scale / math.log(2.0)
