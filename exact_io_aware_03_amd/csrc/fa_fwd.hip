@@ -272,7 +272,7 @@ __device__ __forceinline__ void tile_step(char* smem, int j, const char* kp, con
                                           int krow0, float c_in, const float* kscale, const Dropout& dp, int bh,
                                           const typename QFrag<D, F8>::type& qf, f32x16 (&s)[QH][2],
                                           f32x16 (&sn)[QH][2], f32x16 (&o)[QH][D / 32], float (&m)[QH],
-                                          float (&l)[QH]) {
+                                          float (&l)[QH], uint32_t (&keep)[QH]) {
   using T = Tile<D, F8>;
   const float c = F8 ? c_in * kscale[j] : c_in;
   const int kv0 = j * BC;
@@ -319,8 +319,17 @@ __device__ __forceinline__ void tile_step(char* smem, int j, const char* kp, con
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[qh][kb][i] = fast_exp2(fmaf(s[qh][kb][i], c, -m_use[qh]));
   // ---- phase B: O^T += V^T P^T (MFMA) interleaved with packing and the row sums (VALU) ----
-  uint32_t keep[QH];  // dropout (§2.8): keep bit 8ks + x of key kv0 + 16ks + 8h + x, this lane's row
-  if constexpr (DROP) {
+  // dropout (§2.8): keep[qh] bit 8ks + x is key kv0 + 16ks + 8h + x of this lane's row.
+  // Without the mask the bits are made one tile ahead: the next tile's here, while the P V
+  // MFMAs run (they do not depend on them; 16% faster). With the mask that costs spills and the
+  // bits are made for this tile, just before use.
+  constexpr bool AHEAD = !CAUSAL;
+  uint32_t keep_next[QH];
+  if constexpr (DROP && AHEAD && NEXT) {
+#pragma unroll
+    for (int qh = 0; qh < QH; ++qh) keep_next[qh] = drop_tile_keys(dp, (kv0 + BC + 8 * h) >> 2, q0 + 32 * qh + l32, bh);
+  }
+  if constexpr (DROP && !AHEAD) {
 #pragma unroll
     for (int qh = 0; qh < QH; ++qh) keep[qh] = drop_tile_keys(dp, (kv0 + 8 * h) >> 2, q0 + 32 * qh + l32, bh);
   }
@@ -358,6 +367,10 @@ __device__ __forceinline__ void tile_step(char* smem, int j, const char* kp, con
   }
 #pragma unroll
   for (int qh = 0; qh < QH; ++qh) l[qh] = l[qh] * alpha[qh] + sum32(s[qh][0], s[qh][1]);
+  if constexpr (DROP && AHEAD && NEXT) {
+#pragma unroll
+    for (int qh = 0; qh < QH; ++qh) keep[qh] = keep_next[qh];
+  }
 
   wait_vm_barrier<T::VMCNT>();  // tile j+2 landed; tile j+3 may still be in flight
 }
@@ -456,23 +469,28 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   f32x16 s0[QH][2], s1[QH][2];
   if constexpr (F8) scores_f8<D>(smem, krow0, h, qf, s0);
   else scores<D>(smem, krow0, h, qf, s0);
+  uint32_t keep[QH] = {};  // dropout keep bits of the current tile (tile 0's made here)
+  if constexpr (DROP && !CAUSAL) {
+#pragma unroll
+    for (int qh = 0; qh < QH; ++qh) keep[qh] = drop_tile_keys(a.drop, (8 * h) >> 2, q0 + 32 * qh + l32, bh);
+  }
 
   int j = 0;
   for (; j + 1 < last_w; j += 2) {
     tile_step<D, CAUSAL, true, F8, DROP>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, a.drop, bh, qf, s0, s1,
-                               o, m, l);
+                               o, m, l, keep);
     tile_step<D, CAUSAL, true, F8, DROP>(smem, j + 1, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, a.drop, bh, qf, s1,
-                               s0, o, m, l);
+                               s0, o, m, l, keep);
   }
   if (j < last_w) {
     tile_step<D, CAUSAL, true, F8, DROP>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, a.drop, bh, qf, s0, s1,
-                               o, m, l);
+                               o, m, l, keep);
     ++j;
     tile_step<D, CAUSAL, false, F8, DROP>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, a.drop, bh, qf, s1,
-                                s0, o, m, l);
+                                s0, o, m, l, keep);
   } else {
     tile_step<D, CAUSAL, false, F8, DROP>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, a.drop, bh, qf, s0,
-                                s1, o, m, l);
+                                s1, o, m, l, keep);
   }
   ++j;
   // tiles past this wave's diagonal: keep the workgroup's barrier count
