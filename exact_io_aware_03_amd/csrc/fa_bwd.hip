@@ -112,8 +112,6 @@ __device__ __forceinline__ void wait_vm_barrier() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
-// The same for LDS only: vector-memory operations (prefetches, atomics) stay in flight.
-__device__ __forceinline__ void lds_barrier() { wait_vm_barrier<63>(); }
 
 // This wave's share of the direct-to-LDS loads of `rows` rows of a row-major [*, D] bf16 tensor
 // into a swizzled LDS tile: load p of wave w fills 1 KiB (region kWaves*p + w), lane i landing
@@ -157,26 +155,6 @@ template <int N>
 struct Const {
   static constexpr int value = N;
 };
-
-// A operand of a transposed product read from a row-major LDS tile with two
-// ds_read_b64_tr_b16: lane l receives column c0 + l%32 (c0 = 32*cb) and the 8 consecutive rows
-// 16ks + 8(l/32) .. +7. In each 16-lane group, source lane s points at row r0 + s/4,
-// columns 16((l/16)%2) + 4(s%4) .. +3 of the block.
-template <int ROWB, typename Swz>
-__device__ __forceinline__ bf16x8 tr_frag(const char* base, int ks, int cb, int lane, Swz swz) {
-  const int s = lane & 15, g = lane >> 4;
-  i16x4 r[2];
-#pragma unroll
-  for (int rd = 0; rd < 2; ++rd) {
-    const int row = 16 * ks + 8 * (g >> 1) + 4 * rd + (s >> 2);
-    const int col_b = (32 * cb + 16 * (g & 1) + 4 * (s & 3)) * 2;  // byte column
-    const int off = row * ROWB + (((col_b >> 4) ^ swz(row)) << 4) + (col_b & 15);
-    r[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off));
-  }
-  typedef short i16x8 __attribute__((ext_vector_type(8)));
-  const i16x8 c = __builtin_shufflevector(r[0], r[1], 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, c);
-}
 
 // DROP: the forward's dropout on P (Lecture 21 notes §2.8, exercise 4), its mask regenerated:
 // dV takes P * Z / (1 - p), dP = (dO V^T) * Z / (1 - p), and D = rowsum(dO * O) still holds.

@@ -123,9 +123,6 @@ __device__ __forceinline__ int swap_bits23(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
-// XOR swizzle of 16-byte chunks for row-major LDS tiles read 32 rows at a time through the
-// relabelling above: the 8 rows any 8 consecutive lanes touch land in 8 distinct chunks.
-__device__ __forceinline__ int swz_perm_rows(int row) { return (row & 3) | ((row >> 1) & 4); }
 
 // ---- dropout mask (Lecture 21 notes §2.8: regenerate the mask from the seed) ----
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3",
@@ -154,12 +151,6 @@ __device__ __forceinline__ u32x4 drop_block(const Dropout& dp, int kg, int rg, i
 __device__ __forceinline__ uint32_t drop_bits(const Dropout& dp, uint32_t x) {
   return ((x & 255u) >= dp.t ? 1u : 0u) | (((x >> 8) & 255u) >= dp.t ? 2u : 0u) |
          (((x >> 16) & 255u) >= dp.t ? 4u : 0u) | ((x >> 24) >= dp.t ? 8u : 0u);
-}
-// keep mask (bit c) of the 4 keys 4 kg .. +3 in row `row`
-__device__ __forceinline__ uint32_t drop_keys4(const Dropout& dp, int kg, int row, int bh) {
-  const u32x4 w = drop_block(dp, kg, row >> 2, bh);
-  const int r = row & 3;
-  return drop_bits(dp, r == 0 ? w[0] : r == 1 ? w[1] : r == 2 ? w[2] : w[3]);
 }
 // Value of x in lane S of this lane's quad (DPP quad_perm broadcast).
 template <int S>
@@ -206,14 +197,6 @@ __device__ __forceinline__ uint32_t drop_tile_rows(const Dropout& dp, int rgb, i
   FA_DROP_CALL(0) FA_DROP_CALL(1) FA_DROP_CALL(2) FA_DROP_CALL(3)
 #undef FA_DROP_CALL
   return keep;
-}
-
-// keep mask (bit r) of the 4 rows 4 rg .. +3 for key `key`
-__device__ __forceinline__ uint32_t drop_rows4(const Dropout& dp, int key, int rg, int bh) {
-  const u32x4 w = drop_block(dp, key >> 2, rg, bh);
-  const int sh = 8 * (key & 3);
-  return (((w[0] >> sh) & 255u) >= dp.t ? 1u : 0u) | (((w[1] >> sh) & 255u) >= dp.t ? 2u : 0u) |
-         (((w[2] >> sh) & 255u) >= dp.t ? 4u : 0u) | (((w[3] >> sh) & 255u) >= dp.t ? 8u : 0u);
 }
 
 }  // namespace fa
