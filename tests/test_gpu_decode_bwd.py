@@ -84,7 +84,11 @@ def run_fwd_bwd(inp, causal, scale):
     fa = _fa()
     q, k, v, do = (to_dev(inp[n], "bf16") for n in ("q", "k", "v", "do"))
     o, lse = fa.forward(q, k, v, causal=causal, scale=scale)
-    dq, dk, dv = fa.backward(q, k, v, o, do, lse, causal=causal, scale=scale)
+    B, Nq, Hq, d = q.shape
+    # workspace bytes all 0xFF (NaN as fp32): a row of D the kernels never wrote would show
+    ws = torch.full((fa.fa_bwd_workspace_size(B, Hq, Nq, d),), 255, dtype=torch.uint8, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, causal, scale)
     torch.cuda.synchronize()
     return to_np(dq), to_np(dk), to_np(dv)
 
