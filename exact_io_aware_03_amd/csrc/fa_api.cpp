@@ -227,6 +227,7 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int
   if (!q || !k_cache || !v_cache || !seqlens_k || !o || !lse) return FA_ERR_INVALID_ARG;
   for (const void* p : {q, k_cache, v_cache, (const void*)o, (const void*)lse})
     if (!aligned16(p)) return FA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(seqlens_k) & 3u) != 0) return FA_ERR_INVALID_ARG;
   if (Nq != 1) return FA_ERR_INVALID_ARG;
   int st = common_checks(B, Hq, Hkv, 1, Nk_max, d, scale);
   if (st != FA_OK) return st;
@@ -248,19 +249,23 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int
 
 // ---- planner helpers -------------------------------------------------------------------------
 
+static double wave_efficiency(long n_blocks, long n_cus) {
+  const long waves = (n_blocks + n_cus - 1) / n_cus;
+  return (double)n_blocks / (double)(waves * n_cus);
+}
+
 double fa_wave_efficiency(int n_blocks, int n_cus) {
   if (n_blocks < 1 || n_cus < 1) return 0.0;
-  const long waves = (n_blocks + (long)n_cus - 1) / n_cus;
-  return (double)n_blocks / (double)(waves * n_cus);
+  return wave_efficiency(n_blocks, n_cus);
 }
 
 int fa_plan_splits(int n_blocks, int n_cus, double frac) {
   if (n_blocks < 1 || n_cus < 1 || !(frac > 0.0) || frac > 1.0) return -1;
   constexpr int kMaxSplits = 128;
   double best = 0.0;
-  for (int s = 1; s <= kMaxSplits; ++s) best = std::max(best, fa_wave_efficiency(n_blocks * s, n_cus));
+  for (int s = 1; s <= kMaxSplits; ++s) best = std::max(best, wave_efficiency((long)n_blocks * s, n_cus));
   for (int s = 1; s <= kMaxSplits; ++s)
-    if (fa_wave_efficiency(n_blocks * s, n_cus) >= frac * best) return s;
+    if (wave_efficiency((long)n_blocks * s, n_cus) >= frac * best) return s;
   return 1;
 }
 
@@ -274,6 +279,7 @@ int fa_schedule_makespan(const int* w, int n, int workers, int longest_first, in
     if (w[idx] < 0) return -1;
     const int tgt = (int)(std::min_element(load.begin(), load.end()) - load.begin());  // lowest index on ties
     load[tgt] += w[idx];
+    if (load[tgt] > INT_MAX) return -1;  // a load would not fit the int results
   }
   if (loads_out)
     for (int i = 0; i < workers; ++i) loads_out[i] = (int)load[i];

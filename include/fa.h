@@ -20,10 +20,10 @@
  *   Scale    multiplies the raw scores before the softmax; must be finite and > 0.
  *   dtype    FA_BF16: Q/K/V/O/dO/dQ/dK/dV are bfloat16, accumulation fp32, lse fp32.
  *            FA_F32 : all tensors fp32 (forward only), probabilities kept in fp32.
- *   Memory   every pointer is a device pointer owned by the caller, 16-byte aligned. The
- *            library never allocates or frees memory and holds no state between calls;
- *            scratch space is a caller-provided workspace sized by the *_workspace_size
- *            queries. Calls are thread-safe.
+ *   Memory   every pointer is a device pointer owned by the caller, 16-byte aligned (the
+ *            decode's int32 seqlens_k: 4-byte aligned). The library never allocates or frees
+ *            memory and holds no state between calls; scratch space is a caller-provided
+ *            workspace sized by the *_workspace_size queries. Calls are thread-safe.
  *   Streams  `stream` is a hipStream_t (NULL = default stream). Work is enqueued and the
  *            call returns; buffers must stay valid until the stream has passed it. Results
  *            are defined once the stream is synchronised.
@@ -155,7 +155,7 @@ int fa_plan_splits(int n_blocks, int n_cus, double frac);
 /* Greedy list scheduling of n task lengths onto `workers`: each task goes to the least-loaded
  * worker (lowest index on ties), in arrival order or, with longest_first, longest task first
  * (Lecture 21 notes §4.5, LPT). Writes the final loads to loads_out (may be NULL) and returns
- * the makespan, or -1 on bad arguments. */
+ * the makespan, or -1 on bad arguments (a negative length, or a load above INT_MAX). */
 int fa_schedule_makespan(const int* w, int n, int workers, int longest_first, int* loads_out);
 
 /* Number of (query block, key tile) pairs a causal pass computes for N_q = N_k = n with

@@ -95,6 +95,7 @@ def dec(ws=P, ws_bytes=None, **kw):
 def test_decode_validation():
     assert dec(Nq=2) == INVALID
     assert dec(seqlens=None) == INVALID
+    assert dec(seqlens=ctypes.c_void_p(0x10002)) == INVALID  # int32 lengths not 4-byte aligned
     assert dec(dtype=0) == UNSUPPORTED
     assert dec(Hq=64, Hkv=2) == UNSUPPORTED  # more than 16 query heads per kv head
     assert dec(ws=None) == WORKSPACE
@@ -137,6 +138,8 @@ def test_lpt_pins():
     assert fa.schedule_makespan(p["tasks"], p["workers"], False)[0] == p["natural_makespan"]
     assert fa.schedule_makespan(p["tasks"], p["workers"], True)[0] == p["lpt_makespan"]
     assert -(-sum(p["tasks"]) // p["workers"]) == p["lower_bound"]
+    # a load past INT_MAX is refused rather than wrapped
+    assert fa.schedule_makespan([2**31 - 1, 1], 1, False)[0] == -1
 
 
 def test_causal_tile_count_pin():
