@@ -353,8 +353,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(BwdArgs a) {
   }
   wait_vm_barrier<0>();
   if (qhalf == 0) {
-    // Sum the halves in registers (every read of this slice's area comes before it is
-    // rewritten below; LDS accesses of one wave are ordered).
+    // Sum the halves in registers.
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -362,6 +361,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(BwdArgs a) {
         dk[db][i] = (dk[db][i] + red[((2 * db) * 16 + i) * 64]) * a.scale;
         dv[db][i] += red[((2 * db + 1) * 16 + i) * 64];
       }
+    wave_sync();  // the fp32 reads above come before the bf16 tiles overwrite the area
     // Row-major bf16 tiles [32 keys][D] of dK and dV in this slice's area. Registers i, i+1
     // (i even) hold keys r, r+1 for dim 32db + l32; adjacent lanes swap one value so the even
     // lane packs dims (2m, 2m+1) of key r and the odd lane those of key r+1.
@@ -381,6 +381,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(BwdArgs a) {
         *(uint32_t*)(tile + 32 * ROWB + row * ROWB + col) =
             odd ? pack_bf16x2(sv, dv[db][i + 1]) : pack_bf16x2(dv[db][i], sv);
       }
+    wave_sync();  // every lane's tile writes land before the lanes read each other's rows
     // 16-byte stores of whole row segments; rows past the end of the keys are dropped by the
     // buffer range.
     const long base = ((long)b * a.Nk + kw0) * a.k_row + hk * D;

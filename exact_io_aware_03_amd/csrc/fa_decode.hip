@@ -53,12 +53,6 @@ __device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
   }
   return x;
 }
-// Orders this wave's LDS accesses and keeps the compiler from moving them across the point.
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // Cached length of sequence b, clamped to [1, Nk_max], and its number of 64-key blocks.
 __device__ __forceinline__ int seq_len(const DecArgs& a, int b) { return min(max(a.seqlens[b], 1), a.Nk_max); }

@@ -69,6 +69,18 @@ __device__ __forceinline__ float halves_sum(float x) {
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
+// Ordering point for LDS data handed between lanes of one wave (or for reusing an LDS area
+// through a pointer of another type): the compiler moves no memory access across it, and the
+// wavefront-scope fences make this wave's earlier LDS writes visible to its later reads. The
+// hardware runs one wave's LDS instructions in order, so no workgroup barrier is needed.
+__device__ __forceinline__ void wave_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  asm volatile("" ::: "memory");
+}
+
 // Raw buffer resource covering `bytes` from `base` (out-of-range loads return 0 without a
 // memory access, out-of-range stores are dropped). Word 3 selects 32-bit untyped access.
 // The range check applies to the 32-bit per-lane offset, so callers keep offsets below 2 GiB.
