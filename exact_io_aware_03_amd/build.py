@@ -1,9 +1,14 @@
 """Build libfa.so (HIP for gfx950) in-tree with hipcc.
 
-Usage: python -m exact_io_aware_03_amd.build [--jobs N] [--debug]
+Usage: python -m exact_io_aware_03_amd.build [--jobs N] [--debug] [--sched-strategy NAME]
 
 Every source under csrc/ is compiled for gfx950 with packed-fp32 instruction selection
 disabled, then linked into exact_io_aware_03_amd/libfa.so next to this file.
+
+--sched-strategy builds with one of LLVM's other AMDGPU machine-scheduler strategies (max-ilp,
+max-memory-clause, iterative-ilp, iterative-minreg). Running the GPU tests against such a build
+checks that no kernel depends on an instruction order the compiler is free to change (a missing
+wait or fence); build again without the option afterwards.
 """
 
 from __future__ import annotations
@@ -46,9 +51,11 @@ def _compile(src: str, opt: list[str]) -> str:
     return obj
 
 
-def build(jobs: int = 4, debug: bool = False, verbose: bool = True) -> str:
+def build(jobs: int = 4, debug: bool = False, verbose: bool = True, sched_strategy: str | None = None) -> str:
     os.makedirs(OBJ_DIR, exist_ok=True)
     opt = ["-O1", "-g"] if debug else ["-O3"]
+    if sched_strategy:
+        opt += ["-mllvm", f"-amdgpu-sched-strategy={sched_strategy}"]
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, opt), SOURCES))
     tmp = OUT + ".tmp"
@@ -58,7 +65,7 @@ def build(jobs: int = 4, debug: bool = False, verbose: bool = True) -> str:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, OUT)
     if verbose:
-        print(f"built {OUT}")
+        print(f"built {OUT}" + (f" (scheduler strategy {sched_strategy})" if sched_strategy else ""))
     return OUT
 
 
@@ -66,9 +73,10 @@ if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=4)
     ap.add_argument("--debug", action="store_true")
+    ap.add_argument("--sched-strategy", choices=["max-ilp", "max-memory-clause", "iterative-ilp", "iterative-minreg"])
     args = ap.parse_args()
     try:
-        build(args.jobs, args.debug)
+        build(args.jobs, args.debug, sched_strategy=args.sched_strategy)
     except RuntimeError as e:
         print(e, file=sys.stderr)
         sys.exit(1)
