@@ -114,3 +114,124 @@ def test_rotation_spreads_outliers():
     rms = lambda t: np.sqrt((np.asarray(t, np.float64) ** 2).mean())  # noqa: E731
     assert abs(rms(rq) / rms(q) - 1) < 1e-5
     assert np.abs(q).max() / rms(q) > 3 * np.abs(rq).max() / rms(rq)
+
+
+# ---- the quantiser against exact arithmetic ----------------------------------------------
+
+def _e4m3_values():
+    """The 127 non-negative finite E4M3 values from the format's definition (independent of the
+    oracle's decoder): subnormals m * 2^-9 (m = 0..7), normals (1 + m/8) * 2^(e-7) for
+    e = 1..15, m = 0..7, except e = 15, m = 7 (NaN). Index = code."""
+    vals = [m * 2.0 ** -9 for m in range(8)]
+    vals += [(1 + m / 8) * 2.0 ** (e - 7) for e in range(1, 16) for m in range(8) if not (e == 15 and m == 7)]
+    return np.array(vals)
+
+
+def _exact_quantize(x, signs, block=64):
+    """fp64 quantiser: rotation by J = diag(signs) H_d / sqrt(d) in fp64 (H from scipy's
+    Sylvester construction), exact block maxima, t = y * 448 / amax, nearest E4M3 value by
+    search over the value table with ties to the even code. Returns (codes, t)."""
+    from scipy.linalg import hadamard as sp_hadamard
+
+    x = np.asarray(x, dtype=np.float64)
+    B, N, H, d = x.shape
+    y = x @ (np.diag(signs) @ sp_hadamard(d) / math.sqrt(d)) if signs is not None else x
+    t = np.zeros_like(y)
+    for r0 in range(0, N, block):
+        blk = y[:, r0:r0 + block]
+        amax = np.abs(blk).max(axis=(1, 3))
+        inv = np.where(amax > 0, 448.0 / np.where(amax > 0, amax, 1.0), 1.0)
+        t[:, r0:r0 + block] = blk * inv[:, None, :, None]
+    vals = _e4m3_values()
+    a = np.abs(t).ravel()
+    hi = np.clip(np.searchsorted(vals, a), 1, len(vals) - 1)
+    lo = hi - 1
+    dlo, dhi = a - vals[lo], vals[hi] - a
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    codes = (pick | (np.signbit(t.ravel()).astype(np.int64) << 7)).astype(np.uint8)
+    return codes.reshape(t.shape), t
+
+
+@pytest.mark.parametrize("d,rotate,outliers", [(128, True, 0.0), (128, False, 0.0), (64, True, 0.01),
+                                                (128, True, 0.01)])
+def test_quantize_against_exact_fp64_quantiser(d, rotate, outliers):
+    # The oracle decides each code in fp32 (the order the GPU uses). Against an fp64 quantiser
+    # (exact rotation, exact division by the block scale, nearest-even E4M3) a code may differ
+    # only where the exact scaled value t sits so close to a midpoint between two neighbouring
+    # codes that the fp32 rounding of t crosses it: then the codes are neighbours and the fp32
+    # value and the exact one lie on opposite sides of that midpoint. Such cases must be rare.
+    rng = RNG(40 + d)
+    x = rng.standard_normal((2, 300, 3, d)).astype(np.float32)
+    if outliers:
+        x[rng.random(x.shape) < outliers] *= 20.0
+    signs = rng.choice([-1.0, 1.0], size=d) if rotate else None
+    codes, scales, _ = fp8.quantize(x, signs)
+    exact_codes, t = _exact_quantize(x, signs)
+    # the scales agree with the exact block maxima to fp32 rounding of the rotation
+    y = x.astype(np.float64) @ (np.diag(signs) @ fp8.hadamard(d) / math.sqrt(d)) if rotate else x.astype(np.float64)
+    for i, r0 in enumerate(range(0, 300, 64)):
+        amax = np.abs(y[:, r0:r0 + 64]).max(axis=(1, 3))
+        assert np.all(np.abs(scales[:, :, i] / (amax / 448.0) - 1) < 2.0 ** -18)
+    diff = codes != exact_codes
+    n_diff = int(diff.sum())
+    assert n_diff <= 1e-4 * codes.size, n_diff
+    if n_diff:
+        vals = _e4m3_values()
+        c32, c64 = codes[diff].astype(np.int64), exact_codes[diff].astype(np.int64)
+        assert np.all((c32 >> 7) == (c64 >> 7))                    # same sign
+        assert np.all(np.abs((c32 & 127) - (c64 & 127)) == 1)      # neighbouring codes
+        a = np.abs(t[diff])
+        mid = (vals[np.minimum(c32 & 127, c64 & 127)] + vals[np.maximum(c32 & 127, c64 & 127)]) / 2
+        # t lies within the fp32 error of the scaled values (at most ~1.3e-4 on these inputs,
+        # where the block maximum maps to 448) of a midpoint
+        assert np.all(np.abs(a - mid) <= 2.0 ** -12), np.abs(a - mid).max()
+
+
+# ---- the lecture's own FP8 experiment (§4.4): N = 1024, d = 128, normal + 0.1% large values ----
+
+def _m22_tensor(seed):
+    # "large values" read as x10 (the magnitude the page leaves open; it reproduces the page's
+    # max/RMS of |Q| before the rotation: 26.9 on the page, about 29 here)
+    r = RNG(seed)
+    x = r.standard_normal((1, 1024, 1, 128)).astype(np.float32)
+    x[r.random(x.shape) < 0.001] *= 10.0
+    return x
+
+
+def test_m22_rotation_lowers_max_over_rms_to_the_pages_values():
+    # §4.4: the rotation takes |Q|'s max/RMS from 26.9 to 5.0
+    q = _m22_tensor(1)
+    signs = RNG(5).choice([-1.0, 1.0], size=128)
+    rq = fp8.rotate_f32(q, signs).astype(np.float64)
+    ratio = lambda t: np.abs(t).max() / np.sqrt((np.asarray(t, np.float64) ** 2).mean())  # noqa: E731
+    before, after = ratio(q), ratio(rq)
+    assert 26.9 / 1.25 <= before <= 26.9 * 1.25, before
+    assert 5.0 / 1.25 <= after <= 5.0 * 1.25, after
+
+
+def test_m22_quantisation_error_with_and_without_rotation():
+    # §4.4 on this data: with FP8 Q and K only, the rotation lowers the attention error 2.1x; and
+    # after the rotation, quantisation per block is slightly worse than one scale for the whole
+    # tensor. The oracle quantiser with block = N is the single-scale case. Errors are the RMS
+    # of the output against exact attention on the unquantised inputs, non-causal and causal.
+    from oracle import attention as ora
+
+    q, k, v = (_m22_tensor(s) for s in (1, 2, 3))
+    signs = RNG(5).choice([-1.0, 1.0], size=128)
+    scale = 1 / math.sqrt(128)
+    ratios = []
+    for causal in (False, True):
+        ro, _ = ora.forward(q, k, v, causal, scale)
+        err = {}
+        for rot in (False, True):
+            for block in (64, 1024):
+                qd = fp8.quantize(q, signs if rot else None, block)[2]
+                kd = fp8.quantize(k, signs if rot else None, block)[2]
+                o, _ = ora.forward(qd, kd, v, causal, scale)
+                err[rot, block] = float(np.sqrt(((o - ro) ** 2).mean()))
+        ratios.append(err[False, 1024] / err[True, 1024])
+        # block scales help the unrotated tensor; after the rotation they are no better
+        assert err[False, 64] < err[False, 1024]
+        assert 0.95 * err[True, 1024] <= err[True, 64] <= 1.3 * err[True, 1024]
+    r = float(np.mean(ratios))
+    assert 2.1 / 1.5 <= r <= 2.1 * 1.5, ratios
