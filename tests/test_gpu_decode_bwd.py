@@ -74,7 +74,7 @@ def test_decode_config():
     inp = workloads.make_workload_inputs(w)
     o, lse = run_decode(inp, w.scale)
     ro, rl = ora.decode(inp["q"], inp["k"], inp["v"], inp["seqlens"], w.scale)
-    check("O", o, ro, "bf16")
+    check("O", o, ro, "bf16", config=True)
     check("L", lse, rl, "bf16", is_lse=True)
 
 
@@ -94,22 +94,26 @@ def run_fwd_bwd(inp, causal, scale):
 
 
 @pytest.mark.parametrize(
-    "B,Nq,Nk,Hq,Hkv,d,causal",
+    "B,Nq,Nk,Hq,Hkv,d,causal,seed",
     [
-        (1, 128, 128, 1, 1, 128, False),
-        (1, 128, 128, 1, 1, 128, True),
-        (2, 300, 300, 2, 2, 128, True),   # ragged
-        (1, 200, 200, 4, 2, 64, False),   # GQA, d = 64
-        (1, 257, 257, 4, 1, 128, True),   # GQA 4:1, ragged
-        (1, 64, 64, 2, 2, 64, True),
-        (1, 100, 333, 2, 1, 128, False),  # N_q != N_k, both ragged
-        (1, 520, 70, 2, 1, 64, False),    # more query rows than keys
-        (1, 1, 1, 1, 1, 128, False),      # one query, one key: dS = 0, dV = dO
+        (1, 128, 128, 1, 1, 128, False, None),
+        (1, 128, 128, 1, 1, 128, True, None),
+        (2, 300, 300, 2, 2, 128, True, None),   # ragged
+        (1, 200, 200, 4, 2, 64, False, None),   # GQA, d = 64
+        (1, 257, 257, 4, 1, 128, True, None),   # GQA 4:1, ragged
+        # the same shape at the inputs where the plain 2e-2 bound first failed (dV 0.0224 at
+        # |ref| = 4.73): the dK/dV of a kv head sum four query heads and reach |ref| 7.5
+        (1, 257, 257, 4, 1, 128, True, 1542),
+        (1, 64, 64, 2, 2, 64, True, None),
+        (1, 100, 333, 2, 1, 128, False, None),  # N_q != N_k, both ragged
+        (1, 520, 70, 2, 1, 64, False, None),    # more query rows than keys
+        (1, 1, 1, 1, 1, 128, False, None),      # one query, one key: dS = 0, dV = dO
     ],
 )
-def test_bwd_small(B, Nq, Nk, Hq, Hkv, d, causal):
-    say(f"bwd B={B} Nq={Nq} Nk={Nk} Hq={Hq} Hkv={Hkv} d={d} causal={causal}")
-    seed = 900 + Nq + d if Nq == Nk else 950 + Nq + 3 * Nk + d
+def test_bwd_small(B, Nq, Nk, Hq, Hkv, d, causal, seed):
+    if seed is None:
+        seed = 900 + Nq + d if Nq == Nk else 950 + Nq + 3 * Nk + d
+    say(f"bwd B={B} Nq={Nq} Nk={Nk} Hq={Hq} Hkv={Hkv} d={d} causal={causal} seed={seed}")
     inp = workloads.make_attention_inputs(B, Nq, Nk, Hq, Hkv, d, seed=seed, with_do=True)
     scale = 1.0 / math.sqrt(d)
     dq, dk, dv = run_fwd_bwd(inp, causal, scale)
@@ -129,9 +133,9 @@ def test_bwd_config():
     say(f"  oracle gradients on heads {sel}")
     rq, rk, rv = ora.backward(inp["q"], inp["k"], inp["v"], inp["do"], True, w.scale, heads=sel)
     for b, g in sel:
-        check(f"dQ[b={b},h={g}]", dq[b, :, g], rq[b, :, g], "bf16")
-        check(f"dK[b={b},h={g}]", dk[b, :, g], rk[b, :, g], "bf16")
-        check(f"dV[b={b},h={g}]", dv[b, :, g], rv[b, :, g], "bf16")
+        check(f"dQ[b={b},h={g}]", dq[b, :, g], rq[b, :, g], "bf16", config=True)
+        check(f"dK[b={b},h={g}]", dk[b, :, g], rk[b, :, g], "bf16", config=True)
+        check(f"dV[b={b},h={g}]", dv[b, :, g], rv[b, :, g], "bf16", config=True)
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -146,9 +150,9 @@ def test_bwd_training_shape(causal):
     say(f"  oracle gradients on heads {sel}")
     rq, rk, rv = ora.backward(inp["q"], inp["k"], inp["v"], inp["do"], causal, w.scale, heads=sel)
     for b, g in sel:
-        check(f"dQ[b={b},h={g}]", dq[b, :, g], rq[b, :, g], "bf16")
-        check(f"dK[b={b},h={g}]", dk[b, :, g], rk[b, :, g], "bf16")
-        check(f"dV[b={b},h={g}]", dv[b, :, g], rv[b, :, g], "bf16")
+        check(f"dQ[b={b},h={g}]", dq[b, :, g], rq[b, :, g], "bf16", config=True)
+        check(f"dK[b={b},h={g}]", dk[b, :, g], rk[b, :, g], "bf16", config=True)
+        check(f"dV[b={b},h={g}]", dv[b, :, g], rv[b, :, g], "bf16", config=True)
 
 
 def test_bwd_and_fwd_are_reproducible():

@@ -50,6 +50,7 @@ SMALL = [
     (1, 128, 128, 1, 1, 128, False, 0.25),
     (2, 300, 300, 2, 2, 128, True, 0.25),
     (2, 300, 300, 4, 2, 128, False, 0.25),  # GQA
+    (2, 300, 300, 4, 2, 128, True, 0.5),    # GQA with the mask: the causal K/V-outer path with dropout
     (1, 77, 333, 4, 1, 64, False, 0.125),
     (1, 257, 257, 2, 2, 64, True, 0.25),
 ]
@@ -111,7 +112,7 @@ def test_dropout_training_shape_sampled_heads():
         keep = odp.keep_mask_head(b * w.Hq + h, w.Nq, w.Nk, p, seed, off)[None, None]
         ro, _ = odp.forward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), keep, p, True, w.scale)
         rq, rk, rv = odp.backward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["do"]), keep, p, True, w.scale)
-        check(f"O[b={b},h={h}]", sl(o), ro, "bf16")
-        check(f"dQ[b={b},h={h}]", sl(dq), rq, "bf16")
-        check(f"dK[b={b},h={h}]", sl(dk), rk, "bf16")
-        check(f"dV[b={b},h={h}]", sl(dv), rv, "bf16")
+        check(f"O[b={b},h={h}]", sl(o), ro, "bf16", config=True)
+        check(f"dQ[b={b},h={h}]", sl(dq), rq, "bf16", config=True)
+        check(f"dK[b={b},h={h}]", sl(dk), rk, "bf16", config=True)
+        check(f"dV[b={b},h={h}]", sl(dv), rv, "bf16", config=True)

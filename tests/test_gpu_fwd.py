@@ -127,12 +127,12 @@ def _sampled_config(w, causal, n_heads, n_rows, seed):
     say(f"  oracle on {len(sel)} full heads")
     ro, rl = ora.forward(inp["q"], inp["k"], inp["v"], causal, w.scale, heads=sel)
     for b, h in sel:
-        check(f"O[b={b},h={h}]", o[b, :, h], ro[b, :, h], w.dtype)
+        check(f"O[b={b},h={h}]", o[b, :, h], ro[b, :, h], w.dtype, config=True)
         check(f"L[b={b},h={h}]", lse[b, h], rl[b, h], w.dtype, is_lse=True)
     rows = np.unique(np.concatenate([[0, 1, w.Nq - 1], workloads.sample_indices(w.Nq, n_rows, seed + 1)]))
     say(f"  oracle on {rows.size} rows of every head")
     ro, rl = ora.forward(inp["q"], inp["k"], inp["v"], causal, w.scale, rows=rows)
-    check("O[rows]", o[:, rows], ro[:, rows], w.dtype)
+    check("O[rows]", o[:, rows], ro[:, rows], w.dtype, config=True)
     check("L[rows]", lse[:, :, rows], rl[:, :, rows], w.dtype, is_lse=True)
 
 
