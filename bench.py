@@ -8,10 +8,13 @@ causal mask. `value` is the step's algorithmic TFLOP/s: 4*N_q*N_k*d per head for
 10*N_q*N_k*d for a backward (five products, the recomputation of S included) over the visible
 pairs (N(N+1)/2 with the causal mask). The ragged GQA decode is an inference path of its own
 and is reported in `results` in HBM GB/s, as are the long-context causal forward and the
-causal backward of the backward workload. Every kernel time comes from HIP events on the stream
-the library launches on. The fp64 CPU oracle is timed on a bounded sample of the training-shape
-forward (`cpu_baseline`). Inputs are the seeded synthetic tensors of workloads.py, resident in
-device memory before any timed region. One JSON line on stdout.
+causal backward of the backward workload, and the single-head fp32 forward (against the fp32
+matrix peak). Every kernel time comes from HIP events on the stream the library launches on:
+per part, 10 untimed launches then 50 timed ones, reported as median, minimum and mean (the
+roofline uses the mean launch duration). The fp64 CPU oracle is timed on a bounded sample of the
+training-shape forward (`cpu_baseline`), and on a bounded sample of each of the five workloads
+beside the GPU figures (`cpu_baseline.per_workload`). Inputs are the seeded synthetic tensors of
+workloads.py, resident in device memory before any timed region. One JSON line on stdout.
 """
 
 from __future__ import annotations
@@ -36,6 +39,7 @@ PEAK_FP8_TFLOPS = 5000.0  # MI355X dense fp8 MFMA
 # the FP8 path runs Q K^T (half the FLOPs) on fp8 MFMA and P V on bf16 MFMA
 PEAK_FP8_QK_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
 PEAK_HBM_GBS = 8000.0
+PEAK_F32_TFLOPS = 157.3  # MI355X fp32 matrix (and vector) peak
 
 
 def log(*a):
@@ -66,7 +70,7 @@ def dev(x, dtype="bf16"):
     return t.to(torch.bfloat16) if dtype == "bf16" else t
 
 
-def time_launches(fn, reps, warmup):
+def time_launches(fn, reps=50, warmup=10):
     """Per-launch durations (ms) with HIP events on the current stream (the launch stream)."""
     import torch
 
@@ -80,6 +84,28 @@ def time_launches(fn, reps, warmup):
         b.record()
     torch.cuda.synchronize()
     return [a.elapsed_time(b) for a, b in evs]
+
+
+def stats(ms_list):
+    """median / min / mean of per-launch durations (ms)."""
+    a = np.asarray(ms_list, dtype=np.float64)
+    return {"ms": round(float(np.median(a)), 4), "ms_min": round(float(a.min()), 4),
+            "ms_mean": round(float(a.mean()), 4), "launches": int(a.size)}
+
+
+def rate_entry(ms_list, work, kind):
+    """Result entry for one part: times, and the rate at the median (TFLOP/s or GB/s)."""
+    st = stats(ms_list)
+    if kind == "hbm":
+        gbs = work / (st["ms"] * 1e-3) / 1e9
+        st.update(gbs=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4))
+    else:
+        peak = {"bf16": PEAK_BF16_TFLOPS, "f32": PEAK_F32_TFLOPS, "fp8qk": PEAK_FP8_QK_TFLOPS}[kind]
+        tf = work / (st["ms"] * 1e-3) / 1e12
+        st.update(tflops=round(tf, 2), frac_peak=round(tf / peak, 4))
+        if kind != "bf16":
+            st["peak"] = round(peak, 1)
+    return st
 
 
 def csrc_sha256():
@@ -108,16 +134,26 @@ def measured_traffic(call):
     return int(rec["calls"][call]["traffic_bytes"])
 
 
+def _host_threads():
+    """Threads the oracle's BLAS pool runs with, set to the cores this process may use."""
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+
+        threadpool_limits(limits=cores)
+        used = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        used = cores
+    return cores, int(used)
+
+
 def cpu_baseline(w, budget_s=12.0):
-    """The fp64 oracle, as it stands, on whole heads of the workload until ~budget_s elapse."""
+    """The fp64 oracle, as it stands, on whole heads of the training-shape forward until about
+    budget_s elapse (the headline baseline), then on a bounded sample of each of the five
+    workloads (rates in the workload's own unit, beside the GPU figures)."""
     from oracle import attention as ora
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        cores = 1
+    cores, threads = _host_threads()
     inp = workloads.make_attention_inputs(1, w.Nq, w.Nk, 4, 4, w.d, seed=w.seed, dtype=w.dtype)
     flops, heads, t0 = 0.0, 0, time.perf_counter()
     while True:
@@ -128,11 +164,75 @@ def cpu_baseline(w, budget_s=12.0):
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
+    del inp
     return {
-        "value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+        "value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "host_cores": cores,
         "sample": f"{heads} whole heads (N_q=N_k={w.Nq}, d={w.d}, no mask) of the training-shape forward, "
-                  f"fp64 numpy, {dt:.1f} s",
+                  f"fp64 numpy, {dt:.1f} s, BLAS pool of {threads} threads",
     }
+
+
+def oracle_per_workload():
+    """Oracle rate on a bounded sample of each workload: (sample text, seconds, rate, unit,
+    estimated seconds for the whole workload). Samples: the fp32 forward whole; one head of the
+    training-shape forward with and without the mask; 512 rows of one head of the long-context
+    forward; 8 of the 64 decode sequences; the backward of one head of the backward workload."""
+    from oracle import attention as ora
+
+    out = {}
+    warm = workloads.make_attention_inputs(1, 256, 256, 1, 1, 128, seed=0)
+    ora.forward(warm["q"], warm["k"], warm["v"], False, 0.1)  # BLAS pool start-up, untimed
+
+    def put(name, sample, dt, work, full_work, unit):
+        scale = 1e12 if unit == "TFLOP/s" else 1e9
+        out[name] = {"sample": sample, "s": round(dt, 3), "rate": round(work / dt / scale, 6), "unit": unit,
+                     "est_full_s": round(dt * full_work / work, 1)}
+
+    w1 = workloads.WORKLOADS["fwd_f32_256x64"]
+    inp = workloads.make_workload_inputs(w1)
+    t0 = time.perf_counter()
+    ora.forward(inp["q"], inp["k"], inp["v"], False, w1.scale)
+    fl = fwd_flops(1, 1, w1.Nq, w1.Nk, w1.d, False)
+    put("fwd_f32_256x64", "whole", time.perf_counter() - t0, fl, fl, "TFLOP/s")
+
+    w2 = workloads.WORKLOADS["fwd_bf16_b16h16n2048d128"]
+    inp = workloads.make_attention_inputs(1, w2.Nq, w2.Nk, 1, 1, w2.d, seed=w2.seed)
+    for m in (False, True):
+        t0 = time.perf_counter()
+        ora.forward(inp["q"], inp["k"], inp["v"], m, w2.scale)
+        fl = fwd_flops(1, 1, w2.Nq, w2.Nk, w2.d, m)
+        put("fwd_%s_b16h16n2048d128" % ("causal" if m else "nc"), "one head", time.perf_counter() - t0, fl,
+            fl * w2.B * w2.Hq, "TFLOP/s")
+
+    w3 = workloads.WORKLOADS["fwd_bf16_causal_h32n16384d128"]
+    inp = workloads.make_attention_inputs(1, w3.Nq, w3.Nk, 1, 1, w3.d, seed=w3.seed,
+                                          outlier_frac=w3.outlier_frac, outlier_scale=w3.outlier_scale)
+    rows = np.arange(w3.Nq - 512, w3.Nq)  # the 512 longest rows
+    t0 = time.perf_counter()
+    ora.forward(inp["q"], inp["k"], inp["v"], True, w3.scale, rows=rows)
+    fl = 4.0 * w3.d * float(np.sum(rows + 1))
+    put("fwd_causal_h32n16384d128", "the last 512 rows of one head", time.perf_counter() - t0, fl,
+        fwd_flops(1, w3.Hq, w3.Nq, w3.Nk, w3.d, True), "TFLOP/s")
+
+    w4 = workloads.WORKLOADS["decode_bf16_b64hq32hkv8d128"]
+    lens = np.random.Generator(np.random.PCG64([w4.seed, 1])).integers(
+        w4.len_range[0], w4.len_range[1], endpoint=True, size=w4.B).astype(np.int32)
+    sub = lens[:8]
+    inp = workloads.make_decode_inputs(8, w4.Hq, w4.Hkv, int(sub.max()), w4.d, seed=w4.seed, lengths=sub)
+    t0 = time.perf_counter()
+    ora.decode(inp["q"], inp["k"], inp["v"], inp["seqlens"], w4.scale)
+    by = 2 * w4.Hkv * w4.d * 2 * float(np.sum(sub)) + 8 * w4.Hq * (w4.d * 4 + 4)
+    put("decode_b64hq32hkv8d128", "8 of the 64 sequences", time.perf_counter() - t0, by, decode_bytes(w4, lens),
+        "GB/s")
+
+    w5 = workloads.WORKLOADS["bwd_bf16_causal_b8h16n4096d128"]
+    inp = workloads.make_attention_inputs(1, w5.Nq, w5.Nk, 1, 1, w5.d, seed=w5.seed, with_do=True)
+    t0 = time.perf_counter()
+    ora.backward(inp["q"], inp["k"], inp["v"], inp["do"], True, w5.scale)
+    fl = bwd_flops(1, 1, w5.Nq, w5.d, True)
+    put("bwd_causal_b8h16n4096d128", "one head", time.perf_counter() - t0, fl, fl * w5.B * w5.Hq, "TFLOP/s")
+    return out
 
 
 def main():
@@ -142,7 +242,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="only the training-shape forward step")
-    ap.add_argument("--reps", type=int, default=10, help="timed launches per extra workload")
+    ap.add_argument("--reps", type=int, default=50, help="timed launches per part (after 10 untimed)")
     ap.add_argument("--calib", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -164,6 +264,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    reps = args.reps
 
     # ---- the step: training-shape forward + backward, without and with the causal mask ----
     w = workloads.WORKLOADS["fwd_bf16_b16h16n2048d128"]
@@ -203,138 +304,27 @@ def main():
 
     # ---- per-call times of the step's parts, HIP events on the launch stream ----
     results = {}
-    part_ms = {}
+    part = {}
     for m in (False, True):
         tag = "causal" if m else "nc"
-        f_ms = float(np.mean(time_launches(lambda: fwd(m), args.reps * 2, 3)))
-        b_ms = float(np.mean(time_launches(lambda: bwd(m), args.reps, 2)))
-        part_ms[("fwd", m)], part_ms[("bwd", m)] = f_ms, b_ms
-        for kind, ms, fl in (("fwd", f_ms, ff[m]), ("bwd", b_ms, bf[m])):
-            tf = fl / (ms * 1e-3) / 1e12
-            results[f"{kind}_{tag}_b16h16n2048d128"] = {"ms": round(ms, 4), "tflops": round(tf, 2),
-                                                        "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
-    # the dominant part of the step: the call with the largest share of the step's time
-    dom = max(part_ms, key=part_ms.get)
-    dom_ms = part_ms[dom]
+        for kind, fn, fl in (("fwd", fwd, ff[m]), ("bwd", bwd, bf[m])):
+            t = time_launches(lambda: fn(m), reps)
+            part[(kind, m)] = float(np.mean(t))
+            results[f"{kind}_{tag}_b16h16n2048d128"] = rate_entry(t, fl, "bf16")
+    # the dominant part of the step: the call with the largest share of the step's time; its
+    # roofline figure uses the mean launch duration
+    dom = max(part, key=part.get)
+    dom_ms = part[dom]
     dom_flops = (ff if dom[0] == "fwd" else bf)[dom[1]]
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
     dom_call = "%s %s" % ("fa_fwd" if dom[0] == "fwd" else "fa_bwd", "causal" if dom[1] else "non-causal")
     dom_name = {"fwd": "fwd_bf16_kernel<128,%s>" % ("true" if dom[1] else "false"),
-                "bwd": "fa_bwd %s (bwd_dq_kernel<128> + bwd_main_kernel<128>)" % ("causal" if dom[1] else "non-causal")}[dom[0]]
+                "bwd": "fa_bwd %s (%s)" % ("causal" if dom[1] else "non-causal", BWD_KERNELS)}[dom[0]]
     del q, k, v, do, o, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
 
     if not args.no_extra:
-        # long-context causal forward
-        w3 = workloads.WORKLOADS["fwd_bf16_causal_h32n16384d128"]
-        log(f"[bench] {w3.name}")
-        inp = workloads.make_workload_inputs(w3)
-        q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
-        del inp
-        o = torch.empty_like(q)
-        lse = torch.empty((w3.B, w3.Hq, w3.Nq), dtype=torch.float32, device="cuda")
-        ms = float(np.mean(time_launches(lambda: fa.fa_fwd(q, k, v, o, lse, causal=True, scale=w3.scale),
-                                         args.reps, 2)))
-        tf = fwd_flops(w3.B, w3.Hq, w3.Nq, w3.Nk, w3.d, True) / (ms * 1e-3) / 1e12
-        results["fwd_causal_h32n16384d128"] = {"ms": round(ms, 4), "tflops": round(tf, 2),
-                                               "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
-        del q, k, v, o, lse
-        torch.cuda.empty_cache()
-
-        # decode (HBM bound)
-        w4 = workloads.WORKLOADS["decode_bf16_b64hq32hkv8d128"]
-        log(f"[bench] {w4.name}")
-        inp = workloads.make_workload_inputs(w4)
-        q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
-        lens = torch.from_numpy(inp["seqlens"]).cuda()
-        nbytes = decode_bytes(w4, inp["seqlens"])
-        del inp
-        # three copies of the cache (3 x 2 GiB), used in turn, so no timed call finds the
-        # previous call's rows in the 256 MB last-level cache
-        caches = [(k, v)] + [(k.clone(), v.clone()) for _ in range(2)]
-        o = torch.empty_like(q)
-        lse = torch.empty((w4.B, w4.Hq), dtype=torch.float32, device="cuda")
-        ws = torch.empty(fa.fa_decode_workspace_size(w4.B, w4.Hq, w4.Nk, w4.d), dtype=torch.uint8, device="cuda")
-        turn = [0]
-
-        def decode_call():
-            kc, vc = caches[turn[0] % 3]
-            turn[0] += 1
-            fa.fa_decode(q, kc, vc, lens, o, lse, ws, scale=w4.scale)
-
-        ms = float(np.mean(time_launches(decode_call, args.reps * 2, 3)))
-        gbs = nbytes / (ms * 1e-3) / 1e9
-        results["decode_b64hq32hkv8d128"] = {"ms": round(ms, 4), "gbs": round(gbs, 1),
-                                             "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes}
-        del q, k, v, o, lse, ws, lens, caches
-        torch.cuda.empty_cache()
-
-        # causal backward (dQ kernel + dK/dV kernel), forward untimed
-        w5 = workloads.WORKLOADS["bwd_bf16_causal_b8h16n4096d128"]
-        log(f"[bench] {w5.name}")
-        inp = workloads.make_workload_inputs(w5)
-        q, k, v, do = dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["do"])
-        del inp
-        o, lse = fa.forward(q, k, v, causal=True, scale=w5.scale)
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        ws = torch.empty(fa.fa_bwd_workspace_size(w5.B, w5.Hq, w5.Nq, w5.d), dtype=torch.uint8, device="cuda")
-        ms = float(np.mean(time_launches(
-            lambda: fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, causal=True, scale=w5.scale), args.reps, 2)))
-        tf = bwd_flops(w5.B, w5.Hq, w5.Nq, w5.d, True) / (ms * 1e-3) / 1e12
-        results["bwd_causal_b8h16n4096d128"] = {"ms": round(ms, 4), "tflops": round(tf, 2),
-                                                "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-                                                "tflops_8n2d_convention": round(0.8 * tf, 2)}
-        del q, k, v, do, o, lse, dq, dk, dv, ws
-        torch.cuda.empty_cache()
-
-        # FP8 forward on the training shape: Q and K quantised to E4M3 beforehand (as the kernel
-        # producing them would hand them over), so the timed call is the attention alone; the
-        # quantise pass is timed on its own (HBM bound: 2 bytes read, 1 written per value)
-        log("[bench] fwd_fp8_b16h16n2048d128")
-        inp = workloads.make_attention_inputs(w.B, w.Nq, w.Nk, w.Hq, w.Hkv, w.d, w.seed, w.dtype)
-        q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
-        del inp
-        signs = np.random.Generator(np.random.PCG64(9)).choice([-1.0, 1.0], size=w.d).astype(np.float32)
-        signs = torch.from_numpy(signs).cuda()
-        q8, qs = fa.quantize_fp8(q, signs)
-        k8, ks = fa.quantize_fp8(k, signs)
-        o = torch.empty_like(q)
-        lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda")
-        for m in (False, True):
-            ms = float(np.mean(time_launches(
-                lambda: fa.fa_fwd_fp8(q8, k8, v, qs, ks, o, lse, causal=m, scale=w.scale), args.reps * 2, 3)))
-            tf = ff[m] / (ms * 1e-3) / 1e12
-            results["fwd_fp8_%s_b16h16n2048d128" % ("causal" if m else "nc")] = {
-                "ms": round(ms, 4), "tflops": round(tf, 2), "peak": round(PEAK_FP8_QK_TFLOPS, 1),
-                "frac_peak": round(tf / PEAK_FP8_QK_TFLOPS, 4)}
-        ms = float(np.mean(time_launches(lambda: fa.fa_quantize_fp8(q, signs, q8, qs), args.reps, 2)))
-        qbytes = q.numel() * 3 + qs.numel() * 4
-        results["quantize_fp8_b16h16n2048d128"] = {"ms": round(ms, 4), "gbs": round(qbytes / (ms * 1e-3) / 1e9, 1),
-                                                   "frac_hbm": round(qbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-        del q, k, v, q8, k8, qs, ks, o, lse, signs
-        torch.cuda.empty_cache()
-
-        # dropout on P (p = 0.1) on the training shape without the mask: forward and backward
-        # regenerate the keep mask from (seed, offset); FLOPs counted as without dropout
-        log("[bench] dropout_b16h16n2048d128")
-        inp = workloads.make_attention_inputs(w.B, w.Nq, w.Nk, w.Hq, w.Hkv, w.d, w.seed, w.dtype, with_do=True)
-        q, k, v, do = dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["do"])
-        del inp
-        o = torch.empty_like(q)
-        lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda")
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.Hq, w.Nq, w.d), dtype=torch.uint8, device="cuda")
-        pd, seed = 0.1, 0x5EED
-        f_ms = float(np.mean(time_launches(
-            lambda: fa.fa_fwd_dropout(q, k, v, o, lse, pd, seed, 0, scale=w.scale), args.reps * 2, 3)))
-        b_ms = float(np.mean(time_launches(
-            lambda: fa.fa_bwd_dropout(q, k, v, o, do, lse, dq, dk, dv, ws, pd, seed, 0, scale=w.scale), args.reps, 2)))
-        for kind, ms, fl in (("fwd", f_ms, ff[False]), ("bwd", b_ms, bf[False])):
-            tf = fl / (ms * 1e-3) / 1e12
-            results[f"{kind}_dropout0.1_nc_b16h16n2048d128"] = {"ms": round(ms, 4), "tflops": round(tf, 2),
-                                                               "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
-        del q, k, v, do, o, lse, dq, dk, dv, ws
-        torch.cuda.empty_cache()
+        extra_parts(fa, w, ff, bf, results, reps)
 
     line = {
         "metric": METRIC,
@@ -355,11 +345,135 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(dom_call)},
         "results": results,
+        "build": fa.build_info(),
     }
     if not args.no_cpu:
         log("[bench] cpu baseline (fp64 oracle)")
         line["cpu_baseline"] = cpu_baseline(w)
+        if not args.no_extra:
+            log("[bench] oracle per workload (bounded samples)")
+            per = oracle_per_workload()
+            for name, rec in per.items():
+                gpu = results.get(name)
+                if gpu is not None:
+                    rec["gpu_ms"] = gpu["ms"]
+                    rec["gpu_speedup_est"] = round(rec["est_full_s"] * 1e3 / gpu["ms"], 1)
+            line["cpu_baseline"]["per_workload"] = per
     print(json.dumps(line), flush=True)
+
+
+BWD_KERNELS = "bwd_dq_kernel<128> + bwd_main_kernel<128>"
+
+
+def extra_parts(fa, w, ff, bf, results, reps):
+    """The other workloads (long-context forward, decode, backward workload, fp32 forward) and
+    the next-row paths (FP8 forward, dropout), each timed per launch."""
+    import torch
+
+    # single-head fp32 forward (latency-bound; reported against the fp32 peak)
+    w1 = workloads.WORKLOADS["fwd_f32_256x64"]
+    log(f"[bench] {w1.name}")
+    inp = workloads.make_workload_inputs(w1)
+    q, k, v = dev(inp["q"], "f32"), dev(inp["k"], "f32"), dev(inp["v"], "f32")
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 1, w1.Nq), dtype=torch.float32, device="cuda")
+    t = time_launches(lambda: fa.fa_fwd(q, k, v, o, lse, causal=False, scale=w1.scale), reps)
+    results["fwd_f32_256x64"] = rate_entry(t, fwd_flops(1, 1, w1.Nq, w1.Nk, w1.d, False), "f32")
+    del q, k, v, o, lse
+
+    # long-context causal forward
+    w3 = workloads.WORKLOADS["fwd_bf16_causal_h32n16384d128"]
+    log(f"[bench] {w3.name}")
+    inp = workloads.make_workload_inputs(w3)
+    q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+    del inp
+    o = torch.empty_like(q)
+    lse = torch.empty((w3.B, w3.Hq, w3.Nq), dtype=torch.float32, device="cuda")
+    t = time_launches(lambda: fa.fa_fwd(q, k, v, o, lse, causal=True, scale=w3.scale), reps)
+    results["fwd_causal_h32n16384d128"] = rate_entry(t, fwd_flops(w3.B, w3.Hq, w3.Nq, w3.Nk, w3.d, True), "bf16")
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+
+    # decode (HBM bound)
+    w4 = workloads.WORKLOADS["decode_bf16_b64hq32hkv8d128"]
+    log(f"[bench] {w4.name}")
+    inp = workloads.make_workload_inputs(w4)
+    q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+    lens = torch.from_numpy(inp["seqlens"]).cuda()
+    nbytes = decode_bytes(w4, inp["seqlens"])
+    del inp
+    # three copies of the cache (3 x 2 GiB), used in turn, so no timed call finds the previous
+    # call's rows in the 256 MB last-level cache
+    caches = [(k, v)] + [(k.clone(), v.clone()) for _ in range(2)]
+    o = torch.empty_like(q)
+    lse = torch.empty((w4.B, w4.Hq), dtype=torch.float32, device="cuda")
+    ws = torch.empty(fa.fa_decode_workspace_size(w4.B, w4.Hq, w4.Nk, w4.d), dtype=torch.uint8, device="cuda")
+    turn = [0]
+
+    def decode_call():
+        kc, vc = caches[turn[0] % 3]
+        turn[0] += 1
+        fa.fa_decode(q, kc, vc, lens, o, lse, ws, scale=w4.scale)
+
+    results["decode_b64hq32hkv8d128"] = dict(rate_entry(time_launches(decode_call, reps), nbytes, "hbm"),
+                                             bytes=nbytes)
+    del q, k, v, o, lse, ws, lens, caches
+    torch.cuda.empty_cache()
+
+    # causal backward of the backward workload, forward untimed
+    w5 = workloads.WORKLOADS["bwd_bf16_causal_b8h16n4096d128"]
+    log(f"[bench] {w5.name}")
+    inp = workloads.make_workload_inputs(w5)
+    q, k, v, do = dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["do"])
+    del inp
+    o, lse = fa.forward(q, k, v, causal=True, scale=w5.scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.fa_bwd_workspace_size(w5.B, w5.Hq, w5.Nq, w5.d), dtype=torch.uint8, device="cuda")
+    t = time_launches(lambda: fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, causal=True, scale=w5.scale), reps)
+    e = rate_entry(t, bwd_flops(w5.B, w5.Hq, w5.Nq, w5.d, True), "bf16")
+    e["tflops_8n2d_convention"] = round(0.8 * e["tflops"], 2)
+    results["bwd_causal_b8h16n4096d128"] = e
+    del q, k, v, do, o, lse, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+
+    # FP8 forward on the training shape: Q and K quantised to E4M3 beforehand (as the kernel
+    # producing them would hand them over), so the timed call is the attention alone; the
+    # quantise pass is timed on its own (HBM bound: 2 bytes read, 1 written per value)
+    log("[bench] fwd_fp8_b16h16n2048d128")
+    inp = workloads.make_attention_inputs(w.B, w.Nq, w.Nk, w.Hq, w.Hkv, w.d, w.seed, w.dtype)
+    q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+    del inp
+    signs = np.random.Generator(np.random.PCG64(9)).choice([-1.0, 1.0], size=w.d).astype(np.float32)
+    signs = torch.from_numpy(signs).cuda()
+    q8, qs = fa.quantize_fp8(q, signs)
+    k8, ks = fa.quantize_fp8(k, signs)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda")
+    for m in (False, True):
+        t = time_launches(lambda: fa.fa_fwd_fp8(q8, k8, v, qs, ks, o, lse, causal=m, scale=w.scale), reps)
+        results["fwd_fp8_%s_b16h16n2048d128" % ("causal" if m else "nc")] = rate_entry(t, ff[m], "fp8qk")
+    t = time_launches(lambda: fa.fa_quantize_fp8(q, signs, q8, qs), reps)
+    results["quantize_fp8_b16h16n2048d128"] = rate_entry(t, q.numel() * 3 + qs.numel() * 4, "hbm")
+    del q, k, v, q8, k8, qs, ks, o, lse, signs
+    torch.cuda.empty_cache()
+
+    # dropout on P (p = 0.1) on the training shape without the mask: forward and backward
+    # regenerate the keep mask from (seed, offset); FLOPs counted as without dropout
+    log("[bench] dropout_b16h16n2048d128")
+    inp = workloads.make_attention_inputs(w.B, w.Nq, w.Nk, w.Hq, w.Hkv, w.d, w.seed, w.dtype, with_do=True)
+    q, k, v, do = dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["do"])
+    del inp
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.Hq, w.Nq, w.d), dtype=torch.uint8, device="cuda")
+    pd, seed = 0.1, 0x5EED
+    t = time_launches(lambda: fa.fa_fwd_dropout(q, k, v, o, lse, pd, seed, 0, scale=w.scale), reps)
+    results["fwd_dropout0.1_nc_b16h16n2048d128"] = rate_entry(t, ff[False], "bf16")
+    t = time_launches(lambda: fa.fa_bwd_dropout(q, k, v, o, do, lse, dq, dk, dv, ws, pd, seed, 0, scale=w.scale), reps)
+    results["bwd_dropout0.1_nc_b16h16n2048d128"] = rate_entry(t, bf[False], "bf16")
+    del q, k, v, do, o, lse, dq, dk, dv, ws
+    torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":

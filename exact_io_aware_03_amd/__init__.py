@@ -14,7 +14,10 @@ import math
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libfa.so")
+# FA_LIB_VARIANT=<name> loads libfa_<name>.so, a build with another compiler scheduling strategy
+# (python -m exact_io_aware_03_amd.build --sched-strategy <name>); the default build is libfa.so
+_VARIANT = os.environ.get("FA_LIB_VARIANT", "")
+LIB_PATH = os.path.join(_HERE, f"libfa_{_VARIANT}.so" if _VARIANT else "libfa.so")
 
 FA_F32 = 0
 FA_BF16 = 1
@@ -24,6 +27,7 @@ EXPORTED = (
     "fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_workspace_size", "fa_strerror",
     "fa_version", "fa_wave_efficiency", "fa_plan_splits", "fa_schedule_makespan", "fa_causal_tiles",
     "fa_fp8_scale_count", "fa_quantize_fp8", "fa_fwd_fp8", "fa_fwd_dropout", "fa_bwd_dropout",
+    "fa_lpt_makespan", "fa_build_info",
 )
 
 _lib = None
@@ -59,10 +63,13 @@ def lib() -> ctypes.CDLL:
     L.fa_version.restype = i
     L.fa_wave_efficiency.argtypes = [i, i]
     L.fa_wave_efficiency.restype = ctypes.c_double
-    L.fa_plan_splits.argtypes = [i, i, ctypes.c_double]
+    L.fa_plan_splits.argtypes = [i, i, f]
     L.fa_plan_splits.restype = i
     L.fa_schedule_makespan.argtypes = [ctypes.POINTER(i), i, i, i, ctypes.POINTER(i)]
     L.fa_schedule_makespan.restype = i
+    L.fa_lpt_makespan.argtypes = [ctypes.POINTER(i), i, i, ctypes.POINTER(i)]
+    L.fa_lpt_makespan.restype = i
+    L.fa_build_info.restype = ctypes.c_char_p
     L.fa_causal_tiles.argtypes = [i, i, i]
     L.fa_causal_tiles.restype = ctypes.c_long
     L.fa_fp8_scale_count.argtypes = [i, i, i]
@@ -289,6 +296,18 @@ def schedule_makespan(tasks, workers: int, longest_first: bool):
     loads = (ctypes.c_int * workers)()
     ms = lib().fa_schedule_makespan(arr, n, workers, int(longest_first), loads)
     return ms, list(loads)
+
+
+def lpt_makespan(tasks, workers: int):
+    n = len(tasks)
+    arr = (ctypes.c_int * max(n, 1))(*tasks)
+    loads = (ctypes.c_int * workers)()
+    ms = lib().fa_lpt_makespan(arr, n, workers, loads)
+    return ms, list(loads)
+
+
+def build_info() -> str:
+    return lib().fa_build_info().decode()
 
 
 def causal_tiles(n: int, br: int, bc: int) -> int:

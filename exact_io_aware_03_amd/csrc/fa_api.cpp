@@ -53,6 +53,11 @@ extern "C" {
 
 int fa_version(void) { return FA_VERSION; }
 
+#ifndef FA_BUILD_INFO
+#define FA_BUILD_INFO "unspecified build"
+#endif
+const char* fa_build_info(void) { return FA_BUILD_INFO; }
+
 const char* fa_strerror(int code) {
   switch (code) {
     case FA_OK: return "success";
@@ -259,7 +264,8 @@ double fa_wave_efficiency(int n_blocks, int n_cus) {
   return wave_efficiency(n_blocks, n_cus);
 }
 
-int fa_plan_splits(int n_blocks, int n_cus, double frac) {
+int fa_plan_splits(int n_blocks, int n_cus, float frac_f) {
+  const double frac = (double)frac_f;
   if (n_blocks < 1 || n_cus < 1 || !(frac > 0.0) || frac > 1.0) return -1;
   constexpr int kMaxSplits = 128;
   double best = 0.0;
@@ -284,6 +290,10 @@ int fa_schedule_makespan(const int* w, int n, int workers, int longest_first, in
   if (loads_out)
     for (int i = 0; i < workers; ++i) loads_out[i] = (int)load[i];
   return (int)*std::max_element(load.begin(), load.end());
+}
+
+int fa_lpt_makespan(const int* w, int n, int workers, int* loads_out) {
+  return fa_schedule_makespan(w, n, workers, 1, loads_out);
 }
 
 long fa_causal_tiles(int n, int br, int bc) {

@@ -141,6 +141,9 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v, const float* q_sca
 /* Static text for a status code (for FA_ERR_HIP: the last HIP error seen by this thread). */
 const char* fa_strerror(int code);
 int fa_version(void);
+/* Static text naming how this library was built (target, optimisation level, the compiler's
+ * scheduling strategy), so that measurements can say which build they ran. */
+const char* fa_build_info(void);
 
 /* ---- host planner helpers (pure host code; exported so the scheduling rules can be tested) ---- */
 
@@ -149,14 +152,18 @@ int fa_version(void);
 double fa_wave_efficiency(int n_blocks, int n_cus);
 
 /* Smallest split count s in [1, 128] whose wave efficiency for n_blocks*s blocks is at least
- * frac times the best over that range (Lecture 21 notes §6.1, exercise 11). */
-int fa_plan_splits(int n_blocks, int n_cus, double frac);
+ * frac times the best over that range (Lecture 21 notes §6.1, exercise 11). frac in (0, 1],
+ * else -1. */
+int fa_plan_splits(int n_blocks, int n_cus, float frac);
 
 /* Greedy list scheduling of n task lengths onto `workers`: each task goes to the least-loaded
  * worker (lowest index on ties), in arrival order or, with longest_first, longest task first
  * (Lecture 21 notes §4.5, LPT). Writes the final loads to loads_out (may be NULL) and returns
  * the makespan, or -1 on bad arguments (a negative length, or a load above INT_MAX). */
 int fa_schedule_makespan(const int* w, int n, int workers, int longest_first, int* loads_out);
+
+/* LPT: fa_schedule_makespan with the longest task first (Lecture 21 notes §4.5, exercise 10). */
+int fa_lpt_makespan(const int* w, int n, int workers, int* loads_out);
 
 /* Number of (query block, key tile) pairs a causal pass computes for N_q = N_k = n with
  * br-row query blocks and bc-key tiles, whole tiles above the diagonal skipped (§2.5). */

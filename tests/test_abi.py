@@ -134,12 +134,24 @@ def test_lpt_pins():
     assert loads == p["natural_loads"] and ms == max(p["natural_loads"])
     ms, loads = fa.schedule_makespan(p["tasks"], p["workers"], longest_first=True)
     assert loads == p["lpt_loads"] and ms == max(p["lpt_loads"])
+    assert fa.lpt_makespan(p["tasks"], p["workers"]) == (max(p["lpt_loads"]), p["lpt_loads"])
     p = GOLD["lpt_exercise10"]
+    assert fa.lpt_makespan(p["tasks"], p["workers"])[0] == p["lpt_makespan"]
     assert fa.schedule_makespan(p["tasks"], p["workers"], False)[0] == p["natural_makespan"]
     assert fa.schedule_makespan(p["tasks"], p["workers"], True)[0] == p["lpt_makespan"]
     assert -(-sum(p["tasks"]) // p["workers"]) == p["lower_bound"]
     # a load past INT_MAX is refused rather than wrapped
     assert fa.schedule_makespan([2**31 - 1, 1], 1, False)[0] == -1
+
+
+def test_build_info_names_the_target():
+    info = fa.build_info()
+    assert "gfx950" in info and "sched=" in info
+
+
+def test_plan_splits_rejects_bad_fractions():
+    assert fa.plan_splits(32, 132, 0.0) == -1 and fa.plan_splits(32, 132, 1.5) == -1
+    assert fa.plan_splits(32, 132, 1.0) >= 1
 
 
 def test_causal_tile_count_pin():
