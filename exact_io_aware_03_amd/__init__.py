@@ -21,13 +21,14 @@ LIB_PATH = os.path.join(_HERE, f"libfa_{_VARIANT}.so" if _VARIANT else "libfa.so
 
 FA_F32 = 0
 FA_BF16 = 1
-_STATUS = {0: "FA_OK", -1: "FA_ERR_INVALID_ARG", -2: "FA_ERR_UNSUPPORTED", -3: "FA_ERR_HIP", -4: "FA_ERR_WORKSPACE"}
+_STATUS = {0: "FA_OK", -1: "FA_ERR_INVALID_ARG", -2: "FA_ERR_UNSUPPORTED", -3: "FA_ERR_HIP", -4: "FA_ERR_WORKSPACE",
+           -5: "FA_ERR_SCRATCH"}
 
 EXPORTED = (
     "fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_workspace_size", "fa_strerror",
     "fa_version", "fa_wave_efficiency", "fa_plan_splits", "fa_schedule_makespan", "fa_causal_tiles",
     "fa_fp8_scale_count", "fa_quantize_fp8", "fa_fwd_fp8", "fa_fwd_dropout", "fa_bwd_dropout",
-    "fa_lpt_makespan", "fa_build_info",
+    "fa_lpt_makespan", "fa_build_info", "fa_decode_noalloc",
 )
 
 _lib = None
@@ -58,6 +59,8 @@ def lib() -> ctypes.CDLL:
     L.fa_decode_workspace_size.restype = sz
     L.fa_decode.argtypes = [vp] * 6 + [i] * 6 + [f, i, vp, sz, vp]
     L.fa_decode.restype = i
+    L.fa_decode_noalloc.argtypes = [vp] * 6 + [i] * 6 + [f, i, vp]
+    L.fa_decode_noalloc.restype = i
     L.fa_strerror.argtypes = [i]
     L.fa_strerror.restype = ctypes.c_char_p
     L.fa_version.restype = i
@@ -152,6 +155,16 @@ def fa_decode(q, k_cache, v_cache, seqlens, o, lse, workspace, scale: float | No
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib().fa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o), _ptr(lse), B, Hq, Hkv,
                            Nq, Nk_max, d, scale, _dtype_code(q), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def fa_decode_noalloc(q, k_cache, v_cache, seqlens, o, lse, scale: float | None = None, stream=None) -> None:
+    """fa_decode with its scratch in the library's static per-GPU array (allocates nothing)."""
+    _need_contig(q, k_cache, v_cache, seqlens, o, lse)
+    B, Nq, Hq, d = q.shape
+    Nk_max, Hkv = k_cache.shape[1], k_cache.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    _check(lib().fa_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o), _ptr(lse), B, Hq,
+                                   Hkv, Nq, Nk_max, d, scale, _dtype_code(q), _stream(stream)))
 
 
 def fa_quantize_fp8(x, signs, x8, scales, stream=None) -> None:

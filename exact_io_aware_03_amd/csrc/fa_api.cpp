@@ -65,6 +65,7 @@ const char* fa_strerror(int code) {
     case FA_ERR_UNSUPPORTED: return "unsupported head dimension, dtype or mask combination";
     case FA_ERR_HIP: return g_hip_msg;
     case FA_ERR_WORKSPACE: return "workspace missing or too small";
+    case FA_ERR_SCRATCH: return "the call needs more scratch than the library's static per-GPU array holds";
     default: return "unknown status code";
   }
 }
@@ -220,15 +221,29 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
                     ws_bytes, &dp, stream);
 }
 
-size_t fa_decode_workspace_size(int B, int Hq, int Nk_max, int d) {
-  if (B < 1 || Hq < 1 || Nk_max < 1 || d < 1) return 0;
-  const size_t slots = (size_t)(fa::kDecMaxWorkers + B) * Hq;
-  return align256(slots * d * sizeof(float)) + align256(slots * 2 * sizeof(float)) + (size_t)B * 2 * sizeof(int);
+// Decode scratch layout for `workers` split workers: fp32 partial outputs [(workers + B) * Hq, d],
+// partial (max, sum) pairs [(workers + B) * Hq, 2], then the first and last worker of each
+// sequence [B, 2] (int). Returns the total bytes; fills the three parts when base is given.
+static size_t decode_layout(int workers, int B, int Hq, int d, void* base, fa::DecArgs* a) {
+  const size_t slots = (size_t)(workers + B) * Hq;
+  const size_t o_bytes = align256(slots * d * sizeof(float)), ml_bytes = align256(slots * 2 * sizeof(float));
+  if (base && a) {
+    a->part_o = (float*)base;
+    a->part_ml = (float*)((char*)base + o_bytes);
+    a->seq_w = (int*)((char*)base + o_bytes + ml_bytes);
+  }
+  return o_bytes + ml_bytes + (size_t)B * 2 * sizeof(int);
 }
 
-int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int* seqlens_k, void* o, float* lse,
-              int B, int Hq, int Hkv, int Nq, int Nk_max, int d, float scale, int dtype, void* workspace,
-              size_t ws_bytes, void* stream) {
+size_t fa_decode_workspace_size(int B, int Hq, int Nk_max, int d) {
+  if (B < 1 || Hq < 1 || Nk_max < 1 || d < 1) return 0;
+  return decode_layout(fa::kDecMaxWorkers, B, Hq, d, nullptr, nullptr);
+}
+
+// Validation shared by the decode entry points; fills everything but the scratch pointers.
+static int decode_setup(const void* q, const void* k_cache, const void* v_cache, const int* seqlens_k, void* o,
+                        float* lse, int B, int Hq, int Hkv, int Nq, int Nk_max, int d, float scale, int dtype,
+                        fa::DecArgs& a) {
   if (!q || !k_cache || !v_cache || !seqlens_k || !o || !lse) return FA_ERR_INVALID_ARG;
   for (const void* p : {q, k_cache, v_cache, (const void*)o, (const void*)lse})
     if (!aligned16(p)) return FA_ERR_INVALID_ARG;
@@ -237,18 +252,40 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int
   int st = common_checks(B, Hq, Hkv, 1, Nk_max, d, scale);
   if (st != FA_OK) return st;
   if (dtype != FA_BF16 || Hq / Hkv > 16) return FA_ERR_UNSUPPORTED;
-  const size_t need = fa_decode_workspace_size(B, Hq, Nk_max, d);
-  if (!workspace || ws_bytes < need || !aligned16(workspace)) return FA_ERR_WORKSPACE;
   if ((long)B * Nk_max * Hkv > INT_MAX / 128) return FA_ERR_INVALID_ARG;
-  fa::DecArgs a{};
+  a = fa::DecArgs{};
   a.q = q; a.k = k_cache; a.v = v_cache; a.seqlens = seqlens_k; a.o = o; a.lse = lse;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.Nk_max = Nk_max; a.d = d;
-  const size_t slots = (size_t)(fa::kDecMaxWorkers + B) * Hq;
-  a.part_o = (float*)workspace;
-  a.part_ml = (float*)((char*)workspace + align256(slots * d * sizeof(float)));
-  a.seq_w = (int*)((char*)a.part_ml + align256(slots * 2 * sizeof(float)));
   a.k_row = (long)Hkv * d;
   a.c = scale * 1.4426950408889634f;
+  return FA_OK;
+}
+
+int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int* seqlens_k, void* o, float* lse,
+              int B, int Hq, int Hkv, int Nq, int Nk_max, int d, float scale, int dtype, void* workspace,
+              size_t ws_bytes, void* stream) {
+  fa::DecArgs a;
+  const int st = decode_setup(q, k_cache, v_cache, seqlens_k, o, lse, B, Hq, Hkv, Nq, Nk_max, d, scale, dtype, a);
+  if (st != FA_OK) return st;
+  const size_t need = fa_decode_workspace_size(B, Hq, Nk_max, d);
+  if (!workspace || ws_bytes < need || !aligned16(workspace)) return FA_ERR_WORKSPACE;
+  decode_layout(fa::kDecMaxWorkers, B, Hq, d, workspace, &a);
+  a.max_workers = fa::kDecMaxWorkers;
+  return hip_status(fa::launch_decode(a, (hipStream_t)stream));
+}
+
+int fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int* seqlens_k, void* o,
+                      float* lse, int B, int Hq, int Hkv, int Nq, int Nk_max, int d, float scale, int dtype,
+                      void* stream) {
+  fa::DecArgs a;
+  const int st = decode_setup(q, k_cache, v_cache, seqlens_k, o, lse, B, Hq, Hkv, Nq, Nk_max, d, scale, dtype, a);
+  if (st != FA_OK) return st;
+  if (decode_layout(fa::kDecNoAllocWorkers, B, Hq, d, nullptr, nullptr) > fa::kDecScratchBytes) return FA_ERR_SCRATCH;
+  void* base = nullptr;
+  const hipError_t e = fa::decode_scratch(&base);
+  if (e != hipSuccess) return hip_status(e);
+  decode_layout(fa::kDecNoAllocWorkers, B, Hq, d, base, &a);
+  a.max_workers = fa::kDecNoAllocWorkers;
   return hip_status(fa::launch_decode(a, (hipStream_t)stream));
 }
 

@@ -27,6 +27,13 @@
 #include "fa_device.h"
 #include "fa_internal.h"
 
+#include <mutex>
+
+// Scratch of fa_decode_noalloc: the split partials and the per-sequence split bounds live here
+// instead of in a caller's workspace. One copy per GPU, held until the process ends; host code
+// uses only the device address hipGetSymbolAddress returns for it (decode_scratch below).
+static __device__ __align__(256) unsigned char scratch[fa::kDecScratchBytes];
+
 namespace fa {
 namespace {
 
@@ -334,7 +341,8 @@ hipError_t launch_dg(DecArgs a, hipStream_t s) {
   const long blocks_max = (long)a.B * ((a.Nk_max + kUnit - 1) / kUnit);
   // one workgroup per compute unit, fewer when the padded batch has fewer blocks
   long wg = cus < 1 ? 1 : cus;
-  if (wg > kDecMaxWorkers / S) wg = kDecMaxWorkers / S;
+  const int max_workers = a.max_workers > 0 ? a.max_workers : kDecMaxWorkers;
+  if (wg > max_workers / S) wg = max_workers / S;
   if (wg > (blocks_max + S - 1) / S) wg = (blocks_max + S - 1) / S;
   if (wg < 1) wg = 1;
   a.n_workers = (int)(wg * S);
@@ -356,6 +364,25 @@ hipError_t launch_d(const DecArgs& a, hipStream_t s) {
 
 hipError_t launch_decode(const DecArgs& a, hipStream_t s) {
   return a.d == 128 ? launch_d<128>(a, s) : launch_d<64>(a, s);
+}
+
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // this device's copy of the array
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace fa

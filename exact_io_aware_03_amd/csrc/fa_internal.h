@@ -43,11 +43,12 @@ struct DecArgs {
   const int* seqlens;
   void* o;
   float* lse;
-  float* part_o;   // [kDecMaxWorkers + B, Hq, d] unnormalised partial outputs
-  float* part_ml;  // [kDecMaxWorkers + B, Hq, 2] partial (max, sum) in base-2 units
+  float* part_o;   // [max_workers + B, Hq, d] unnormalised partial outputs
+  float* part_ml;  // [max_workers + B, Hq, 2] partial (max, sum) in base-2 units
   int* seq_w;      // [B, 2] first and last worker that covered each sequence
   int B, Hq, Hkv, G, Nk_max, d;
   int n_workers;   // set by the launcher: workers sharing the block list
+  int max_workers; // cap on n_workers (the partial slots are sized for max_workers + B per head)
   long k_row;
   float c;
 };
@@ -81,6 +82,8 @@ constexpr int kFwdF32Rows = 128;  // query rows per fp32 forward workgroup (4 wa
 constexpr int kFwdKeys = 64;      // keys per forward K/V tile
 constexpr int kFwdF32Keys = 32;   // keys per tile in the fp32 forward
 constexpr int kDecMaxWorkers = 2048;  // decode workers (partials per sequence boundary)
+constexpr int kDecNoAllocWorkers = 256;  // worker cap of the decode that allocates nothing
+constexpr size_t kDecScratchBytes = size_t(32) << 20;  // its static per-GPU scratch array
 constexpr int kBwdKeys = 128;     // keys per dK/dV workgroup (4 key slices x 32)
 constexpr int kBwdRows = 64;      // query rows per dK/dV inner step
 constexpr int kBwdDqRows = 256;   // query rows per dQ workgroup (8 waves x 32)
@@ -95,6 +98,9 @@ constexpr int kFp8Block = 64;     // rows per FP8 quantisation block (one scale 
 hipError_t launch_quantize_fp8(const void* x, const float* signs, void* x8, float* scales, int B, int N, int H,
                                int d, hipStream_t s);
 hipError_t launch_decode(const DecArgs& a, hipStream_t s);
+// Device address of the static decode scratch array (kDecScratchBytes) on the current device;
+// looked up once per device.
+hipError_t decode_scratch(void** ptr);
 hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t s);
 
 }  // namespace fa

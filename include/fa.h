@@ -50,7 +50,8 @@ enum fa_status {
   FA_ERR_INVALID_ARG = -1, /* null pointer, size < 1, H_q % H_kv != 0, bad scale, misalignment */
   FA_ERR_UNSUPPORTED = -2, /* d not in {64, 128}, dtype not supported by the call, causal with N_q != N_k */
   FA_ERR_HIP = -3,         /* a kernel launch failed */
-  FA_ERR_WORKSPACE = -4    /* workspace pointer null or smaller than the size query returned */
+  FA_ERR_WORKSPACE = -4,   /* workspace pointer null or smaller than the size query returned */
+  FA_ERR_SCRATCH = -5      /* fa_decode_noalloc: the problem needs more than the static scratch array */
 };
 
 /*
@@ -111,6 +112,20 @@ size_t fa_decode_workspace_size(int B, int Hq, int Nk_max, int d);
 int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int* seqlens_k, void* o,
               float* lse, int B, int Hq, int Hkv, int Nq, int Nk_max, int d, float scale, int dtype,
               void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Decode for callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. Same arguments and result as fa_decode minus
+ * the workspace. The split partials and split bounds live in a fixed 32 MiB device array inside
+ * the library (one per GPU, held until the process ends), and at most 256 workers share the
+ * block list. A problem whose scratch, (256 + B) * Hq * (d + 2) * 4 + 8 * B bytes with each part
+ * rounded up to 256 bytes, exceeds the array returns FA_ERR_SCRATCH before any HIP call. The
+ * call allocates nothing. Every call on a GPU uses that GPU's one array: calls that overlap on
+ * one GPU (on two streams, or from two threads) race and must be serialised by the caller.
+ */
+int fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int* seqlens_k, void* o,
+                      float* lse, int B, int Hq, int Hkv, int Nq, int Nk_max, int d, float scale, int dtype,
+                      void* stream);
 
 /* ---- FP8 forward (Lecture 21 notes §4.4 and exercise 8; "Flash Attention 3/4 笔记" §4) ----
  * Q and K in OCP E4M3 (one byte per value) with one fp32 scale per 64-row block of each

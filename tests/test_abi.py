@@ -104,8 +104,28 @@ def test_decode_validation():
     assert fa.fa_decode_workspace_size(2, 8, 300, 128) >= 2 * 8 * 2 * (128 + 2) * 4
 
 
+def dec_noalloc(**kw):
+    a = dict(B=2, Hq=8, Hkv=2, Nq=1, Nk=300, d=128, scale=0.1, dtype=1)
+    a.update(kw)
+    return fa.lib().fa_decode_noalloc(P, P, P, kw.get("seqlens", P), P, P, a["B"], a["Hq"], a["Hkv"], a["Nq"],
+                                      a["Nk"], a["d"], a["scale"], a["dtype"], None)
+
+
+def test_decode_noalloc_validation_and_scratch_limit():
+    # the same argument checks as fa_decode, then the static scratch limit, all before any HIP call:
+    # (256 + B) * Hq * (d + 2) * 4 bytes (+ 8 B) must fit in 32 MiB
+    assert dec_noalloc(Nq=2) == INVALID
+    assert dec_noalloc(seqlens=None) == INVALID
+    assert dec_noalloc(dtype=0) == UNSUPPORTED
+    assert dec_noalloc(Hq=64, Hkv=2) == UNSUPPORTED
+    SCRATCH = -5
+    assert dec_noalloc(B=2000, Hq=32, Hkv=8) == SCRATCH  # (2256 * 32 * 130 * 4) B > 32 MiB
+    assert dec_noalloc(B=64, Hq=256, Hkv=16) == SCRATCH  # (320 * 256 * 130 * 4) B > 32 MiB
+    assert b"static" in fa.lib().fa_strerror(SCRATCH)
+
+
 def test_strerror_names_every_code():
-    for c in (0, -1, -2, -3, -4):
+    for c in (0, -1, -2, -3, -4, -5):
         assert fa.lib().fa_strerror(c)
     assert b"unknown" in fa.lib().fa_strerror(5)
 

@@ -1,0 +1,48 @@
+"""fa_decode_noalloc (the decode that allocates nothing: its scratch is a static per-GPU array
+in the library) through the C ABI against fa_decode with a workspace, on two calls in a row,
+the second smaller, so the second call finds the first call's contents in the array."""
+
+import math
+
+import numpy as np
+import pytest
+
+import workloads
+from gpu_util import check, say, to_dev, to_np
+from oracle import attention as ora
+
+pytestmark = pytest.mark.gpu
+
+
+def _pair(fa, inp, scale):
+    import torch
+
+    q, k, v = (to_dev(inp[n], "bf16") for n in ("q", "k", "v"))
+    lens = torch.from_numpy(inp["seqlens"]).cuda()
+    B, _, Hq, d = q.shape
+    ws = torch.empty(fa.fa_decode_workspace_size(B, Hq, k.shape[1], d), dtype=torch.uint8, device="cuda")
+    o1, o2 = torch.empty_like(q), torch.empty_like(q)
+    l1 = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    l2 = torch.empty_like(l1)
+    fa.fa_decode(q, k, v, lens, o1, l1, ws, scale)
+    fa.fa_decode_noalloc(q, k, v, lens, o2, l2, scale)
+    torch.cuda.synchronize()
+    return (to_np(o1), to_np(l1)), (to_np(o2), to_np(l2))
+
+
+def test_decode_noalloc_matches_decode_twice():
+    import exact_io_aware_03_amd as fa
+
+    w = workloads.WORKLOADS["decode_bf16_b64hq32hkv8d128"]
+    big = workloads.make_workload_inputs(w)
+    small = workloads.make_decode_inputs(3, 8, 2, 700, 128, seed=9, lengths=[1, 300, 700])
+    for name, inp, scale in (("decode workload", big, w.scale), ("small GQA 4:1", small, 1 / math.sqrt(128))):
+        say(f"noalloc {name}: B={inp['q'].shape[0]} Hq={inp['q'].shape[2]} Hkv={inp['k'].shape[2]}")
+        (o1, l1), (o2, l2) = _pair(fa, inp, scale)
+        say(f"  identical to fa_decode: O {np.array_equal(o1, o2)}, L {np.array_equal(l1, l2)}")
+        check("O noalloc vs fa_decode", o2, o1, "bf16")
+        check("L noalloc vs fa_decode", l2, l1, "bf16", is_lse=True)
+        if inp["q"].shape[0] <= 8:
+            ro, rl = ora.decode(inp["q"], inp["k"], inp["v"], inp["seqlens"], scale)
+            check("O noalloc vs oracle", o2, ro, "bf16")
+            check("L noalloc vs oracle", l2, rl, "bf16", is_lse=True)
