@@ -407,7 +407,7 @@ def extra_parts(fa, w, ff, bf, results, reps):
     caches = [(k, v)] + [(k.clone(), v.clone()) for _ in range(2)]
     o = torch.empty_like(q)
     lse = torch.empty((w4.B, w4.Hq), dtype=torch.float32, device="cuda")
-    ws = torch.empty(fa.fa_decode_workspace_size(w4.B, w4.Hq, w4.Nk, w4.d), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(fa.fa_decode_workspace_size(w4.B, w4.Hq, w4.Nk, w4.d), dtype=torch.uint8, device="cuda")
     turn = [0]
 
     def decode_call():

@@ -243,7 +243,8 @@ def decode(q, k_cache, v_cache, seqlens, scale: float | None = None, stream=None
     import torch
 
     B, _, Hq, d = q.shape
-    ws = torch.empty(fa_decode_workspace_size(B, Hq, k_cache.shape[1], d), dtype=torch.uint8, device=q.device)
+    # zero-filled: the arrival counters at its start must be zero before a first use
+    ws = torch.zeros(fa_decode_workspace_size(B, Hq, k_cache.shape[1], d), dtype=torch.uint8, device=q.device)
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     fa_decode(q, k_cache, v_cache, seqlens, o, lse, ws, scale, stream)

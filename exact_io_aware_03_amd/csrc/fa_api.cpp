@@ -221,18 +221,20 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
                     ws_bytes, &dp, stream);
 }
 
-// Decode scratch layout for `workers` split workers: fp32 partial outputs [(workers + B) * Hq, d],
-// partial (max, sum) pairs [(workers + B) * Hq, 2], then the first and last worker of each
-// sequence [B, 2] (int). Returns the total bytes; fills the three parts when base is given.
+// Decode scratch layout for `workers` split workers: the arrival counters of the split
+// sequences [B * Hq] (int, room for B * Hkv; zero between calls), then the fp32 partial outputs
+// [(workers + B) * Hq, d] and partial (max, sum) pairs [(workers + B) * Hq, 2]. Returns the total
+// bytes; fills the three parts when base is given.
 static size_t decode_layout(int workers, int B, int Hq, int d, void* base, fa::DecArgs* a) {
   const size_t slots = (size_t)(workers + B) * Hq;
+  const size_t c_bytes = align256((size_t)B * Hq * sizeof(int));
   const size_t o_bytes = align256(slots * d * sizeof(float)), ml_bytes = align256(slots * 2 * sizeof(float));
   if (base && a) {
-    a->part_o = (float*)base;
-    a->part_ml = (float*)((char*)base + o_bytes);
-    a->seq_w = (int*)((char*)base + o_bytes + ml_bytes);
+    a->arrive = (int*)base;
+    a->part_o = (float*)((char*)base + c_bytes);
+    a->part_ml = (float*)((char*)base + c_bytes + o_bytes);
   }
-  return o_bytes + ml_bytes + (size_t)B * 2 * sizeof(int);
+  return c_bytes + o_bytes + ml_bytes;
 }
 
 size_t fa_decode_workspace_size(int B, int Hq, int Nk_max, int d) {
@@ -253,6 +255,8 @@ static int decode_setup(const void* q, const void* k_cache, const void* v_cache,
   if (st != FA_OK) return st;
   if (dtype != FA_BF16 || Hq / Hkv > 16) return FA_ERR_UNSUPPORTED;
   if ((long)B * Nk_max * Hkv > INT_MAX / 128) return FA_ERR_INVALID_ARG;
+  // the partials are addressed with 32-bit buffer offsets
+  if ((long)(fa::kDecMaxWorkers + B) * Hq * d * 4 >= (1L << 31)) return FA_ERR_UNSUPPORTED;
   a = fa::DecArgs{};
   a.q = q; a.k = k_cache; a.v = v_cache; a.seqlens = seqlens_k; a.o = o; a.lse = lse;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.Nk_max = Nk_max; a.d = d;

@@ -1,10 +1,11 @@
-// Single-query decode against ragged KV caches: split-KV partials + logsumexp combine.
+// Single-query decode against ragged KV caches: split-KV partials + logsumexp merge.
 //
 // Method (Lecture 21 notes, CMU 11-868: §6.1 Flash-Decoding splits K/V along the sequence,
-// each split produces a partial (m, l, o) and a small kernel merges them by the rescaling
-// rule of §2.2; exercise 3: the merge is associative and commutative, so any split and any
-// merge order give the same result up to rounding; §6.2 GQA packing: the query heads that
-// share a K/V head are stacked as rows of one tile so K/V are read once per group).
+// each split produces a partial (m, l, o) and the partials are merged by the rescaling rule of
+// §2.2, with nothing to merge when a sequence was not split; exercise 3: the merge is
+// associative and commutative, so any split and any merge order give the same result up to
+// rounding; §6.2 GQA packing: the query heads that share a K/V head are stacked as rows of one
+// tile so K/V are read once per group).
 //
 // gfx950 mapping: a persistent grid, one workgroup per compute unit. The work is the list of
 // 64-key blocks of all sequences in order (sequence 0's blocks, then sequence 1's, ...); it is
@@ -17,12 +18,13 @@
 // waves. Each wave walks its range one 64-key block at a time with whole-row 16-byte loads;
 // K is staged through LDS into MFMA operand order, S^T = K Q^T for the packed query heads comes
 // from v_mfma_f32_16x16x32_bf16 (query heads as the 16 MFMA columns), the online softmax and
-// the P V product run on the VALU (each lane owns D/16 head dims of one key in four). A wave
-// writes one fp32 partial (o, m, l) per (kv head, sequence it touched): a worker's ranges and
-// the sequences both advance monotonically through the block list, so (worker + sequence)
-// numbers the partials without collisions. The workers that hold a sequence's first and last
-// blocks record themselves, and the combine kernel merges the partials of the workers in
-// between for each (sequence, query head).
+// the P V product run on the VALU (each lane owns D/16 head dims of one key in four). A job is
+// (kv head, sequence the range touches). When one worker covers the sequence whole, it writes O
+// and L itself. Otherwise it writes a partial (o, m, l) into slot (worker + sequence) -- a
+// worker's ranges and the sequences both advance monotonically through the block list, so no
+// two jobs share a slot -- and counts its arrival on the (sequence, kv head) counter; the last
+// of the sequence's workers to arrive resets the counter and merges the partials of all of
+// them in worker order, so the result does not depend on which one finishes last.
 // Decode is bound by HBM: every cached K/V byte is read exactly once.
 #include "fa_device.h"
 #include "fa_internal.h"
@@ -64,6 +66,62 @@ __device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
 // Cached length of sequence b, clamped to [1, Nk_max], and its number of 64-key blocks.
 __device__ __forceinline__ int seq_len(const DecArgs& a, int b) { return min(max(a.seqlens[b], 1), a.Nk_max); }
 __device__ __forceinline__ int seq_blocks(int n) { return (n + kUnit - 1) / kUnit; }
+
+// Cache policy of the partials' loads and stores: sc1, coherent across the XCDs' L2 caches
+// (the workers that write a sequence's partials and the one that merges them may run on any).
+constexpr int kCoherent = 16;
+
+// Merge the partials of sequence b for the G query heads hq0 .. hq0 + G - 1, written by the
+// workers w_first .. w_last into slots (worker + b): O = sum_c 2^(m_c - M) o_c / l,
+// l = sum_c 2^(m_c - M) l_c, L = (M + log2 l) ln 2, with M the running maximum (Lecture 21 §6.1,
+// exercise 3), in worker order. 64 / GM lanes per head, each owning D * GM / 64 dims; four
+// partials' loads are in flight at a time.
+template <int D, int GM>
+__device__ __forceinline__ void merge_partials(const DecArgs& a, int b, int hq0, int w_first, int w_last, int lane) {
+  constexpr int LPH = 64 / GM;  // lanes per head (GM is a power of two >= G)
+  constexpr int DPL = D / LPH;  // dims per lane
+  const int g = lane / LPH, d0 = (lane % LPH) * DPL;
+  const bool live = g < a.G;
+  const long hq = (long)hq0 + (live ? g : 0);
+  const long slots = (long)(a.n_workers + a.B) * a.Hq;
+  const rsrc_t ro = make_rsrc(a.part_o, slots * D * 4), rm = make_rsrc(a.part_ml, slots * 2 * 4);
+  float mm = kNegInf, ll = 0.f, oo[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) oo[e] = 0.f;
+  for (int w0 = w_first; w0 <= w_last; w0 += 4) {
+    float mc[4], lc[4], oc[4][DPL];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const long slot = ((long)min(w0 + i, w_last) + b) * a.Hq + hq;  // past w_last: re-read, unused
+      // (the builtins return the loaded bits as integers: reinterpret, do not convert; whole
+      // 16-byte vectors are reinterpreted at once, since element-wise reinterpretation of an
+      // integer vector loaded this way was compiled to one element for all)
+      mc[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rm, (int)(slot * 8), 0, kCoherent));
+      lc[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rm, (int)(slot * 8 + 4), 0, kCoherent));
+#pragma unroll
+      for (int e = 0; e < DPL; e += 4) {
+        const f32x4 t = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, (int)((slot * D + d0 + e) * 4), 0, kCoherent));
+#pragma unroll
+        for (int x = 0; x < 4; ++x) oc[i][e + x] = t[x];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (w0 + i > w_last) break;
+      const float mn = fmaxf(mm, mc[i]);
+      const float f_old = fast_exp2(mm - mn), f_new = fast_exp2(mc[i] - mn);  // mm = -inf at first: 0
+      ll = ll * f_old + lc[i] * f_new;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) oo[e] = oo[e] * f_old + oc[i][e] * f_new;
+      mm = mn;
+    }
+  }
+  if (!live) return;
+  __bf16* op = (__bf16*)a.o + ((long)b * a.Hq + hq) * D + d0;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) op[e] = (__bf16)(oo[e] / ll);
+  if (lane % LPH == 0) a.lse[(long)b * a.Hq + hq] = (mm + __log2f(ll)) * kLn2;
+}
 
 // D: head dim (64 or 128). GM: query heads per kv head the registers are sized for. NW: waves
 // per workgroup (8 when GM = 4; 4 for the larger groups, whose accumulators need a SIMD's
@@ -152,12 +210,11 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_partial_kernel(DecArgs a) {
     const int n = seq_len(a, b);
     const int lo = max(u0, pb), hi = min(u1, pb + seq_blocks(n));
     const int k_lo = (lo - pb) * kUnit, k_hi = min(n, (hi - pb) * kUnit);
-    // the workers holding a sequence's first and last blocks record themselves
-    if (hw == 0 && lane == 0) {
-      if (lo == pb) a.seq_w[2 * b] = vw;
-      if (hi == pb + seq_blocks(n)) a.seq_w[2 * b + 1] = vw;
-    }
     const long slot = (long)vw + b;
+    // the workers that cover this sequence: those holding its first and last blocks and all
+    // between (worker w holds blocks [w U / W, (w + 1) U / W))
+    const int w_first = (int)(((long)(pb + 1) * W - 1) / U);
+    const int w_last = (int)(((long)(pb + seq_blocks(n)) * W - 1) / U);
     for (int hk = hw; hk < a.Hkv; hk += Hw) {
       const uint16_t* kp = (const uint16_t*)a.k + (long)b * a.Nk_max * a.k_row + hk * D;
       const uint16_t* vp = (const uint16_t*)a.v + (long)b * a.Nk_max * a.k_row + hk * D;
@@ -275,60 +332,71 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_partial_kernel(DecArgs a) {
         wave_sync();  // p and alpha are read before the next block is staged over them
       }
 
-      // ---- the job's partial: merge the four key groups of the wave, write (o, m, l) ----
+      // ---- end of the job: merge the four key groups of the wave; the only worker of the
+      //      sequence writes O and L, otherwise the partial (o, m, l) goes out and the last of
+      //      the sequence's workers to arrive merges them all ----
       l = xor_sum(l);
 #pragma unroll
-      for (int g = 0; g < GM; ++g) {
+      for (int g = 0; g < GM; ++g)
 #pragma unroll
         for (int e = 0; e < VE; ++e) acc[g][e] = xor_sum(acc[g][e]);
-        if (g4 == 0 && g < G) {
-          float* po = a.part_o + ((slot * a.Hq) + hq0 + g) * D + l16 * VE;
+      // lane l16 < G holds m and l of query head hq0 + l16, and every lane with that l16 the
+      // dims [VE l16, +VE) of all G heads
+      if (w_first == w_last) {
+        // Lecture 21 §6.1: a sequence that was not split needs no merge
+        if (g4 == 0) {
 #pragma unroll
-          for (int e = 0; e < VE; e += 4) *(f32x4*)(po + e) = f32x4{acc[g][e], acc[g][e + 1], acc[g][e + 2], acc[g][e + 3]};
+          for (int g = 0; g < GM; ++g) {
+            const float lg = __shfl(l, g);
+            if (g < G) {
+              uint32_t w[VE / 2];
+#pragma unroll
+              for (int e = 0; e < VE / 2; ++e) w[e] = pack_bf16x2(acc[g][2 * e] / lg, acc[g][2 * e + 1] / lg);
+              uint16_t* op = (uint16_t*)a.o + ((long)b * a.Hq + hq0 + g) * D + l16 * VE;
+              if constexpr (VE == 8) *(u32x4*)op = u32x4{w[0], w[1], w[2], w[3]};
+              else *(u32x2*)op = u32x2{w[0], w[1]};
+            }
+          }
+          if (l16 < G) a.lse[(long)b * a.Hq + hq0 + l16] = (m + __log2f(l)) * kLn2;
         }
+        continue;
       }
-      if (g4 == 0 && l16 < G) {
-        float* pm = a.part_ml + ((slot * a.Hq) + hq0 + l16) * 2;
-        pm[0] = m;
-        pm[1] = l;
+      // partials are stored with agent-scope coherence (write-through past this XCD's L2) so
+      // that the merging worker, wherever it runs, reads them from the coherent level
+      if (g4 == 0) {
+        const long slots = (long)(a.n_workers + a.B) * a.Hq;
+        const rsrc_t ro = make_rsrc(a.part_o, slots * D * 4), rm = make_rsrc(a.part_ml, slots * 2 * 4);
+#pragma unroll
+        for (int g = 0; g < GM; ++g) {
+          if (g < G) {
+            const int off = (int)((((slot * a.Hq) + hq0 + g) * D + l16 * VE) * 4);
+#pragma unroll
+            for (int e = 0; e < VE; e += 4)
+              __builtin_amdgcn_raw_buffer_store_b128(f32x4{acc[g][e], acc[g][e + 1], acc[g][e + 2], acc[g][e + 3]}, ro,
+                                                     off + e * 4, 0, kCoherent);
+          }
+        }
+        if (l16 < G)
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(m), __float_as_uint(l)}, rm,
+                                                (int)(((slot * a.Hq) + hq0 + l16) * 8), 0, kCoherent);
       }
-    }
-    pb += seq_blocks(n);
+      // The stores are complete at the coherent level before the arrival is counted, and the
+      // last arriver reads the partials with agent-coherent loads after its count came back;
+      // that is the release/acquire pair, without the whole-cache write-back and invalidation
+      // an agent-scope fence would cost (measured: the call took 1.55x as long with them).
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      int* cnt = a.arrive + (long)b * a.Hkv + hk;
+      int before = 0;
+      if (lane == 0) before = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      before = __builtin_amdgcn_readfirstlane(__shfl(before, 0));
+      if (before != w_last - w_first) continue;
+      // the last to arrive: reset the counter for the next call and merge the partials of the
+      // workers w_first .. w_last in that order (the result does not depend on who is last)
+      if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      merge_partials<D, GM>(a, b, hq0, w_first, w_last, lane);
+    }    pb += seq_blocks(n);
     if (++b >= a.B || pb >= u1) break;
   }
-}
-
-// Merge the partials of one (sequence, query head), written by the workers first..last that
-// covered the sequence into slots (worker + sequence): O = sum_c 2^(m_c - M) o_c / l,
-// l = sum_c 2^(m_c - M) l_c, L = (M + log2 l) ln 2, with M the running maximum.
-template <int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(DecArgs a) {
-  const int b = blockIdx.x / a.Hq, hq = blockIdx.x % a.Hq;
-  const int w_first = a.seq_w[2 * b], w_last = a.seq_w[2 * b + 1];
-  const int dd = threadIdx.x;
-  float mm = kNegInf, ll = 0.f, oo = 0.f;
-  // four partials' loads in flight at a time (indices past w_last re-read w_last, unused)
-  for (int w0 = w_first; w0 <= w_last; w0 += 4) {
-    float mc[4], lc[4], oc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const long slot = ((long)min(w0 + i, w_last) + b) * a.Hq + hq;
-      mc[i] = a.part_ml[slot * 2];
-      lc[i] = a.part_ml[slot * 2 + 1];
-      oc[i] = a.part_o[slot * D + dd];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (w0 + i > w_last) break;
-      const float mn = fmaxf(mm, mc[i]);
-      const float f_old = fast_exp2(mm - mn), f_new = fast_exp2(mc[i] - mn);  // mm = -inf at first: 0
-      ll = ll * f_old + lc[i] * f_new;
-      oo = oo * f_old + oc[i] * f_new;
-      mm = mn;
-    }
-  }
-  ((__bf16*)a.o)[((long)b * a.Hq + hq) * D + dd] = (__bf16)(oo / ll);
-  if (dd == 0) a.lse[(long)b * a.Hq + hq] = (mm + __log2f(ll)) * kLn2;
 }
 
 template <int D, int GM, int NW>
@@ -347,9 +415,6 @@ hipError_t launch_dg(DecArgs a, hipStream_t s) {
   if (wg < 1) wg = 1;
   a.n_workers = (int)(wg * S);
   hipLaunchKernelGGL((decode_partial_kernel<D, GM, NW>), dim3((unsigned)wg), dim3(NW * 64), 0, s, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.Hq), dim3(D), 0, s, a);
   return hipGetLastError();
 }
 

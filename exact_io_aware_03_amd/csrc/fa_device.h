@@ -69,6 +69,13 @@ __device__ __forceinline__ float halves_sum(float x) {
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
+// A read-only fp32 array seen through the constant address space: uniform indexing then
+// becomes a scalar load (s_load), counted by lgkmcnt, so it neither waits for nor delays the
+// vector-memory loads in flight (a vector load here would make the compiler drain vmcnt).
+// Only for arrays that no kernel of the launch writes.
+typedef const __attribute__((address_space(4))) float cfloat;
+__device__ __forceinline__ cfloat* as_cfloat(const float* p) { return (cfloat*)p; }
+
 // Ordering point for LDS data handed between lanes of one wave (or for reusing an LDS area
 // through a pointer of another type): the compiler moves no memory access across it, and the
 // wavefront-scope fences make this wave's earlier LDS writes visible to its later reads. The

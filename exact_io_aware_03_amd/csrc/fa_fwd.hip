@@ -291,7 +291,7 @@ __device__ __forceinline__ bf16x8 v_frag(const char* vt, int ks, int db, int lan
 template <int D, bool CAUSAL, bool NEXT, bool F8, bool DROP>
 __device__ __forceinline__ void tile_step(char* smem, int j, const char* kp, const char* vp, long k_row, int nk_load,
                                           int nk, const TileDma<D, F8>& dm, int q0, int l32, int h, int lane,
-                                          int krow0, float c_in, const float* kscale, const Dropout& dp, int bh,
+                                          int krow0, float c_in, cfloat* kscale, const Dropout& dp, int bh,
                                           const typename QFrag<D, F8>::type& qf, f32x16 (&s)[QH][2],
                                           f32x16 (&sn)[QH][2], f32x16 (&o)[QH][D / 32], float (&m)[QH],
                                           float (&l)[QH], uint32_t (&keep)[QH]) {
@@ -429,7 +429,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   // (bf16) or [64ks + 32h, +32) (E4M3).
   typename QFrag<D, F8>::type qf;
   float cw = a.c;             // scale * log2(e), times the Q block scale on the FP8 path
-  const float* ksc = nullptr;  // K block scales of this (batch, kv head), FP8 path
+  cfloat* ksc = nullptr;  // K block scales of this (batch, kv head), FP8 path (scalar loads)
   if constexpr (F8) {
     const char* qp8 = (const char*)a.q + (long)b * a.Nq * a.q_row + hq * D;
     const rsrc_t rq = make_rsrc(qp8, (long)(a.Nq - 1) * a.q_row + D);
@@ -444,7 +444,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
       }
     // rows past N (last workgroup) take the last block's scale; their output is dropped
     cw *= a.q_scale[((long)b * a.Hq + hq) * a.q_nblk + min(q0 / kFp8Block, a.q_nblk - 1)];
-    ksc = a.k_scale + ((long)b * a.Hkv + hk) * a.k_nblk;
+    ksc = as_cfloat(a.k_scale + ((long)b * a.Hkv + hk) * a.k_nblk);
   } else {
     const rsrc_t rq = make_rsrc(qp, q_valid);
 #pragma unroll

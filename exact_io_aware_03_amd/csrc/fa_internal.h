@@ -45,7 +45,7 @@ struct DecArgs {
   float* lse;
   float* part_o;   // [max_workers + B, Hq, d] unnormalised partial outputs
   float* part_ml;  // [max_workers + B, Hq, 2] partial (max, sum) in base-2 units
-  int* seq_w;      // [B, 2] first and last worker that covered each sequence
+  int* arrive;     // [B, Hkv] arrival counters of the split sequences; zero between calls
   int B, Hq, Hkv, G, Nk_max, d;
   int n_workers;   // set by the launcher: workers sharing the block list
   int max_workers; // cap on n_workers (the partial slots are sized for max_workers + B per head)

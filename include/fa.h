@@ -95,8 +95,11 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
                    float scale, float p_drop, unsigned long long seed, unsigned int offset, void* workspace,
                    size_t ws_bytes, void* stream);
 
-/* Workspace bytes fa_decode needs: fp32 partials (o, m, l) for up to 2048 + B splits of every
- * query head, and two ints per sequence naming the first and last split that covered it. */
+/* Workspace bytes fa_decode needs: arrival counters of the split sequences (ceil256(4 * B * Hq)
+ * bytes at the start), then fp32 partials (o, m, l) for up to 2048 + B splits of every query
+ * head. The counters must be zero before a workspace's first use (allocate it zero-filled once);
+ * every call leaves them zero again, so a workspace is reused without clearing. The rest of the
+ * workspace needs no initial contents. */
 size_t fa_decode_workspace_size(int B, int Hq, int Nk_max, int d);
 
 /*
@@ -104,10 +107,12 @@ size_t fa_decode_workspace_size(int B, int Hq, int Nk_max, int d);
  * q [B,1,Hq,d]; k_cache, v_cache [B,Nk_max,Hkv,d]; seqlens_k int32 [B] on the device: sequence b
  * attends its first seqlens_k[b] cached keys (values are clamped to [1, Nk_max]; rows past the
  * length are never read). The 64-key blocks of all sequences, in order, are cut into equal
- * contiguous ranges, one per worker of a persistent grid; a worker's piece of a sequence yields a
- * partial (m, l, o) for the H_q/H_kv query heads that share a kv head, and a second kernel merges
- * each sequence's partials by logsumexp. Nq must be 1; dtype FA_BF16; H_q/H_kv <= 16.
- * o [B,1,Hq,d] bf16, lse fp32 [B,Hq].
+ * contiguous ranges, one per worker of a persistent grid. A sequence that one worker covers
+ * whole is finished by that worker; otherwise each worker's piece yields a partial (m, l, o) for
+ * the H_q/H_kv query heads that share a kv head, and the last of the sequence's workers to
+ * finish merges them by logsumexp in worker order (the result does not depend on timing). Nq
+ * must be 1; dtype FA_BF16; H_q/H_kv <= 16. o [B,1,Hq,d] bf16, lse fp32 [B,Hq]. Two calls that
+ * share a workspace must not overlap (one stream, or synchronised).
  */
 int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int* seqlens_k, void* o,
               float* lse, int B, int Hq, int Hkv, int Nq, int Nk_max, int d, float scale, int dtype,
@@ -116,9 +121,10 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int
 /*
  * Decode for callers that cannot allocate device memory: code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc. Same arguments and result as fa_decode minus
- * the workspace. The split partials and split bounds live in a fixed 32 MiB device array inside
- * the library (one per GPU, held until the process ends), and at most 256 workers share the
- * block list. A problem whose scratch, (256 + B) * Hq * (d + 2) * 4 + 8 * B bytes with each part
+ * the workspace. The arrival counters and split partials live in a fixed 32 MiB device array
+ * inside the library (one per GPU, zero when the library loads, held until the process ends;
+ * every call leaves the counters zero), and at most 256 workers share the block list. A problem
+ * whose scratch, 4 * B * Hq + (256 + B) * Hq * (d + 2) * 4 bytes with each of the three parts
  * rounded up to 256 bytes, exceeds the array returns FA_ERR_SCRATCH before any HIP call. The
  * call allocates nothing. Every call on a GPU uses that GPU's one array: calls that overlap on
  * one GPU (on two streams, or from two threads) race and must be serialised by the caller.

@@ -113,7 +113,7 @@ def dec_noalloc(**kw):
 
 def test_decode_noalloc_validation_and_scratch_limit():
     # the same argument checks as fa_decode, then the static scratch limit, all before any HIP call:
-    # (256 + B) * Hq * (d + 2) * 4 bytes (+ 8 B) must fit in 32 MiB
+    # 4 B Hq + (256 + B) * Hq * (d + 2) * 4 bytes must fit in 32 MiB
     assert dec_noalloc(Nq=2) == INVALID
     assert dec_noalloc(seqlens=None) == INVALID
     assert dec_noalloc(dtype=0) == UNSUPPORTED
@@ -183,14 +183,14 @@ def test_causal_tile_count_pin():
 
 
 def test_decode_workspace_size():
-    # fp32 partials (o, then m and l) for 2048 + B splits of every query head, each array padded
-    # to 256 bytes, then the first and last worker of each sequence (int32)
+    # int32 arrival counters (B * Hq), then fp32 partials (o, then m and l) for 2048 + B splits of
+    # every query head, each part padded to 256 bytes
     def pad(x):
         return (x + 255) // 256 * 256
 
     for B, Hq, d in [(64, 32, 128), (1, 1, 64), (3, 5, 128)]:
         slots = (2048 + B) * Hq
-        assert fa.lib().fa_decode_workspace_size(B, Hq, 8192, d) == pad(slots * d * 4) + pad(slots * 8) + B * 8
+        assert fa.lib().fa_decode_workspace_size(B, Hq, 8192, d) == pad(B * Hq * 4) + pad(slots * d * 4) + pad(slots * 8)
     assert fa.lib().fa_decode_workspace_size(0, 32, 8192, 128) == 0
 
 

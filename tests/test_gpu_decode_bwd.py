@@ -25,12 +25,17 @@ def run_decode(inp, scale):
     q, k, v = (to_dev(inp[n], "bf16") for n in ("q", "k", "v"))
     lens = torch.from_numpy(inp["seqlens"]).cuda()
     B, _, Hq, d = q.shape
-    # workspace bytes all 0xFF (NaN as fp32): a read of a partial the kernels never wrote shows
+    # partial area all 0xFF (NaN as fp32): a read of a partial the kernels never wrote shows; the
+    # arrival counters at the start of the workspace are zero, as the contract asks
     ws = torch.full((fa.fa_decode_workspace_size(B, Hq, k.shape[1], d),), 255, dtype=torch.uint8, device="cuda")
+    n_cnt = (B * Hq * 4 + 255) // 256 * 256
+    ws[:n_cnt] = 0
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
     fa.fa_decode(q, k, v, lens, o, lse, ws, scale)
     torch.cuda.synchronize()
+    # every call leaves the counters zero
+    assert int(ws[:n_cnt].count_nonzero()) == 0
     return to_np(o), to_np(lse)
 
 
@@ -66,6 +71,27 @@ def test_decode_small(B, Hq, Hkv, Nk_max, d, lengths):
     ro, rl = ora.decode(inp["q"], inp["k"], inp["v"], inp["seqlens"], scale)
     check("O", o, ro, "bf16")
     check("L", lse, rl, "bf16", is_lse=True)
+
+
+def test_decode_reuses_its_workspace():
+    # two calls on one workspace, the second with other lengths: the counters the first call
+    # leaves (zero) serve the second, and both results match the oracle
+    import torch
+
+    fa = _fa()
+    B, Hq, Hkv, Nk_max, d = 6, 16, 4, 3000, 128
+    ws = torch.zeros(fa.fa_decode_workspace_size(B, Hq, Nk_max, d), dtype=torch.uint8, device="cuda")
+    for lengths, seed in (([3000, 1, 2999, 64, 1500, 700], 801), ([5, 3000, 3000, 129, 1, 2048], 802)):
+        inp = workloads.make_decode_inputs(B, Hq, Hkv, Nk_max, d, seed=seed, lengths=lengths)
+        q, k, v = (to_dev(inp[n], "bf16") for n in ("q", "k", "v"))
+        lens = torch.from_numpy(inp["seqlens"]).cuda()
+        o = torch.empty_like(q)
+        lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+        fa.fa_decode(q, k, v, lens, o, lse, ws, 1 / math.sqrt(d))
+        torch.cuda.synchronize()
+        ro, rl = ora.decode(inp["q"], inp["k"], inp["v"], inp["seqlens"], 1 / math.sqrt(d))
+        check("O", to_np(o), ro, "bf16")
+        check("L", to_np(lse), rl, "bf16", is_lse=True)
 
 
 def test_decode_config():

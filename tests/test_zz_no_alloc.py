@@ -20,7 +20,7 @@ def _pair(fa, inp, scale):
     q, k, v = (to_dev(inp[n], "bf16") for n in ("q", "k", "v"))
     lens = torch.from_numpy(inp["seqlens"]).cuda()
     B, _, Hq, d = q.shape
-    ws = torch.empty(fa.fa_decode_workspace_size(B, Hq, k.shape[1], d), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(fa.fa_decode_workspace_size(B, Hq, k.shape[1], d), dtype=torch.uint8, device="cuda")
     o1, o2 = torch.empty_like(q), torch.empty_like(q)
     l1 = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
     l2 = torch.empty_like(l1)
