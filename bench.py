@@ -275,7 +275,7 @@ def main():
     o = {m: torch.empty_like(q) for m in (False, True)}
     lse = {m: torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda") for m in (False, True)}
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.Hq, w.Nq, w.d), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(fa.fa_bwd_workspace_size(w.B, w.Hq, w.Nq, w.d), dtype=torch.uint8, device="cuda")
 
     def fwd(m):
         fa.fa_fwd(q, k, v, o[m], lse[m], causal=m, scale=w.scale)
@@ -428,11 +428,30 @@ def extra_parts(fa, w, ff, bf, results, reps):
     del inp
     o, lse = fa.forward(q, k, v, causal=True, scale=w5.scale)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(fa.fa_bwd_workspace_size(w5.B, w5.Hq, w5.Nq, w5.d), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(fa.fa_bwd_workspace_size(w5.B, w5.Hq, w5.Nq, w5.d), dtype=torch.uint8, device="cuda")
     t = time_launches(lambda: fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, causal=True, scale=w5.scale), reps)
     e = rate_entry(t, bwd_flops(w5.B, w5.Hq, w5.Nq, w5.d, True), "bf16")
     e["tflops_8n2d_convention"] = round(0.8 * e["tflops"], 2)
     results["bwd_causal_b8h16n4096d128"] = e
+    # the single-pass backward (dQ summed across key blocks in the workspace) on the same call
+    t = time_launches(lambda: fa.fa_bwd_single_pass(q, k, v, o, do, lse, dq, dk, dv, ws, causal=True,
+                                                    scale=w5.scale), reps)
+    results["bwd_single_pass_causal_b8h16n4096d128"] = rate_entry(t, bwd_flops(w5.B, w5.Hq, w5.Nq, w5.d, True), "bf16")
+    del q, k, v, do, o, lse, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+
+    # the single-pass backward on the training shape, both masks
+    log("[bench] bwd_single_pass_b16h16n2048d128")
+    inp = workloads.make_attention_inputs(w.B, w.Nq, w.Nk, w.Hq, w.Hkv, w.d, w.seed, w.dtype, with_do=True)
+    q, k, v, do = dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["do"])
+    del inp
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.zeros(fa.fa_bwd_workspace_size(w.B, w.Hq, w.Nq, w.d), dtype=torch.uint8, device="cuda")
+    for m in (False, True):
+        o, lse = fa.forward(q, k, v, causal=m, scale=w.scale)
+        t = time_launches(lambda: fa.fa_bwd_single_pass(q, k, v, o, do, lse, dq, dk, dv, ws, causal=m,
+                                                        scale=w.scale), reps)
+        results[f"bwd_single_pass_{'causal' if m else 'nc'}_b16h16n2048d128"] = rate_entry(t, bf[m], "bf16")
     del q, k, v, do, o, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
 
@@ -466,7 +485,7 @@ def extra_parts(fa, w, ff, bf, results, reps):
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.Hq, w.Nq, w.d), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(fa.fa_bwd_workspace_size(w.B, w.Hq, w.Nq, w.d), dtype=torch.uint8, device="cuda")
     pd, seed = 0.1, 0x5EED
     t = time_launches(lambda: fa.fa_fwd_dropout(q, k, v, o, lse, pd, seed, 0, scale=w.scale), reps)
     results["fwd_dropout0.1_nc_b16h16n2048d128"] = rate_entry(t, ff[False], "bf16")

@@ -28,7 +28,7 @@ EXPORTED = (
     "fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_workspace_size", "fa_strerror",
     "fa_version", "fa_wave_efficiency", "fa_plan_splits", "fa_schedule_makespan", "fa_causal_tiles",
     "fa_fp8_scale_count", "fa_quantize_fp8", "fa_fwd_fp8", "fa_fwd_dropout", "fa_bwd_dropout",
-    "fa_lpt_makespan", "fa_build_info", "fa_decode_noalloc",
+    "fa_lpt_makespan", "fa_build_info", "fa_decode_noalloc", "fa_bwd_single_pass",
 )
 
 _lib = None
@@ -55,6 +55,8 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd_workspace_size.restype = sz
     L.fa_bwd.argtypes = [vp] * 9 + [i] * 7 + [f, i, vp, sz, vp]
     L.fa_bwd.restype = i
+    L.fa_bwd_single_pass.argtypes = [vp] * 9 + [i] * 7 + [f, i, vp, sz, vp]
+    L.fa_bwd_single_pass.restype = i
     L.fa_decode_workspace_size.argtypes = [i, i, i, i]
     L.fa_decode_workspace_size.restype = sz
     L.fa_decode.argtypes = [vp] * 6 + [i] * 6 + [f, i, vp, sz, vp]
@@ -135,16 +137,24 @@ def fa_fwd(q, k, v, o, lse, causal: bool = False, scale: float | None = None, st
                         scale, _dtype_code(q), _stream(stream)))
 
 
-def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool = False, scale: float | None = None,
-           stream=None) -> None:
+def _bwd_call(fn, q, k, v, o, dout, lse, dq, dk, dv, workspace, causal, scale, stream) -> None:
     _need_contig(q, k, v, o, dout, lse, dq, dk, dv, workspace)
     B, Nq, Hq, d = q.shape
     Nk, Hkv = k.shape[1], k.shape[2]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check(lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
-                        B, Hq, Hkv, Nq, Nk, d, int(causal), scale, _dtype_code(q), _ptr(workspace), ws_bytes,
-                        _stream(stream)))
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+              B, Hq, Hkv, Nq, Nk, d, int(causal), scale, _dtype_code(q), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool = False, scale: float | None = None,
+           stream=None) -> None:
+    _bwd_call(lib().fa_bwd, q, k, v, o, dout, lse, dq, dk, dv, workspace, causal, scale, stream)
+
+
+def fa_bwd_single_pass(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool = False,
+                       scale: float | None = None, stream=None) -> None:
+    _bwd_call(lib().fa_bwd_single_pass, q, k, v, o, dout, lse, dq, dk, dv, workspace, causal, scale, stream)
 
 
 def fa_decode(q, k_cache, v_cache, seqlens, o, lse, workspace, scale: float | None = None, stream=None) -> None:
@@ -233,7 +243,7 @@ def backward(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = 
     import torch
 
     B, Nq, Hq, d = q.shape
-    ws = torch.empty(fa_bwd_workspace_size(B, Hq, Nq, d), dtype=torch.uint8, device=q.device)
+    ws = torch.zeros(fa_bwd_workspace_size(B, Hq, Nq, d), dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, causal, scale, stream)
     return dq, dk, dv
@@ -267,7 +277,7 @@ def backward_dropout(q, k, v, o, dout, lse, p: float, seed: int, offset: int = 0
     import torch
 
     B, Nq, Hq, d = q.shape
-    ws = torch.empty(fa_bwd_workspace_size(B, Hq, Nq, d), dtype=torch.uint8, device=q.device)
+    ws = torch.zeros(fa_bwd_workspace_size(B, Hq, Nq, d), dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     fa_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, ws, p, seed, offset, causal, scale, stream)
     return dq, dk, dv

@@ -160,15 +160,35 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v, const float* q_sca
   return hip_status(fa::launch_fwd_fp8(a, d, (hipStream_t)stream));
 }
 
+// Backward workspace: the single pass's task-pool counters and its fp32 dQ partial sums (a
+// 64-row x d block per query head and 64-row query block), both zero between calls, then
+// D = rowsum(dO * O) [B, Hq, Nq]. Returns the total bytes; fills the parts when a is given.
+static size_t bwd_zeroed_bytes(int B, int Hq, int Nq, int d) {
+  const size_t blocks = (size_t)B * Hq * ((Nq + fa::kBwdRows - 1) / fa::kBwdRows);
+  return align256(fa::kBwdPoolCounters * sizeof(int)) + blocks * fa::kBwdRows * d * sizeof(float);
+}
+
+static size_t bwd_layout(int B, int Hq, int Nq, int d, void* base, fa::BwdArgs* a) {
+  const size_t z_bytes = bwd_zeroed_bytes(B, Hq, Nq, d);
+  const size_t d_bytes = align256((size_t)B * Hq * Nq * sizeof(float));
+  if (a) {
+    char* p = (char*)base;
+    a->ctr = (int*)p;
+    a->dq_acc = (float*)(p + align256(fa::kBwdPoolCounters * sizeof(int)));
+    a->dvec = (float*)(p + z_bytes);
+  }
+  return z_bytes + d_bytes;
+}
+
 size_t fa_bwd_workspace_size(int B, int Hq, int Nq, int d) {
   if (B < 1 || Hq < 1 || Nq < 1 || d < 1) return 0;
-  return align256((size_t)B * Hq * Nq * sizeof(float));  // D = rowsum(dO * O)
+  return bwd_layout(B, Hq, Nq, d, nullptr, nullptr);
 }
 
 static int bwd_common(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                       void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
                       float scale, int dtype, void* workspace, size_t ws_bytes, const fa::Dropout* drop,
-                      void* stream) {
+                      bool single_pass, void* stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
   for (const void* p : {q, k, v, o, dout, (const void*)lse, (const void*)dq, (const void*)dk, (const void*)dv})
     if (!aligned16(p)) return FA_ERR_INVALID_ARG;
@@ -183,7 +203,7 @@ static int bwd_common(const void* q, const void* k, const void* v, const void* o
   fa::BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
   a.dq = dq; a.dk = dk; a.dv = dv;
-  a.dvec = (float*)workspace;
+  bwd_layout(B, Hq, Nq, d, workspace, &a);
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.G = Hq / Hkv;
   a.q_row = (long)Hq * d;
   a.k_row = (long)Hkv * d;
@@ -194,8 +214,13 @@ static int bwd_common(const void* q, const void* k, const void* v, const void* o
   a.n_qblk_dq = (Nq + fa::kBwdDqRows - 1) / fa::kBwdDqRows;
   const long tasks = (long)B * Hkv * a.n_kvblk, tasks_dq = (long)B * Hq * a.n_qblk_dq;
   if (tasks > INT_MAX || tasks_dq > INT_MAX || (long)B * Nq * Hq > INT_MAX / 4) return FA_ERR_INVALID_ARG;
+  if ((long)B * Hq * ((Nq + fa::kBwdRows - 1) / fa::kBwdRows) * 8 > INT_MAX / 2) return FA_ERR_INVALID_ARG;  // tiles
   a.n_tasks = (int)tasks;
   a.n_tasks_dq = (int)tasks_dq;
+  if (single_pass) {
+    if (!fa::bwd_single_pass_supported(a, d)) return FA_ERR_UNSUPPORTED;
+    return hip_status(fa::launch_bwd_single_pass(a, d, (hipStream_t)stream));
+  }
   if (drop && drop->t > 0) {
     a.drop = *drop;
     return hip_status(fa::launch_bwd_dropout(a, d, (hipStream_t)stream));
@@ -207,7 +232,14 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
            int dtype, void* workspace, size_t ws_bytes, void* stream) {
   return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, causal, scale, dtype, workspace,
-                    ws_bytes, nullptr, stream);
+                    ws_bytes, nullptr, false, stream);
+}
+
+int fa_bwd_single_pass(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                       const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                       int causal, float scale, int dtype, void* workspace, size_t ws_bytes, void* stream) {
+  return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, causal, scale, dtype, workspace,
+                    ws_bytes, nullptr, true, stream);
 }
 
 int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
@@ -218,7 +250,7 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
   const int st = make_dropout(p_drop, seed, offset, dp);
   if (st != FA_OK) return st;
   return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, causal, scale, FA_BF16, workspace,
-                    ws_bytes, &dp, stream);
+                    ws_bytes, &dp, false, stream);
 }
 
 // Decode scratch layout for `workers` split workers: the arrival counters of the split

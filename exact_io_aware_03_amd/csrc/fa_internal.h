@@ -64,6 +64,11 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* dvec;    // D = rowsum(dO * O), [B, Hq, Nq]
+  // single pass only: fp32 dQ partial sums with adder tags (one 4 KiB tile per query head,
+  // 64-row block and wave; zero between calls) and the task-pool counters (zero between calls)
+  float* dq_acc;
+  int* ctr;
+  int n_pools;
   int B, Hq, Hkv, Nq, Nk, G;
   long q_row, k_row;
   float scale;
@@ -88,6 +93,7 @@ constexpr int kBwdKeys = 128;     // keys per dK/dV workgroup (4 key slices x 32
 constexpr int kBwdRows = 64;      // query rows per dK/dV inner step
 constexpr int kBwdDqRows = 256;   // query rows per dQ workgroup (8 waves x 32)
 constexpr int kBwdDqKeys = 64;    // keys per dQ K/V tile
+constexpr int kBwdPoolCounters = 16;  // single-pass backward: 8 task pools, a done count, padding
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, hipStream_t s);
@@ -102,5 +108,9 @@ hipError_t launch_decode(const DecArgs& a, hipStream_t s);
 // looked up once per device.
 hipError_t decode_scratch(void** ptr);
 hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t s);
+// The single-pass backward (d = 128): all five products in one key-block-outer pass, dQ summed in
+// the workspace in a fixed order. Supported shapes: bwd_single_pass_supported.
+bool bwd_single_pass_supported(const BwdArgs& a, int d);
+hipError_t launch_bwd_single_pass(const BwdArgs& a, int d, hipStream_t s);
 
 }  // namespace fa

@@ -63,7 +63,13 @@ enum fa_status {
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
            int Nq, int Nk, int d, int causal, float scale, int dtype, void* stream);
 
-/* Workspace bytes fa_bwd needs: D = rowsum(dO * O), fp32 [B, Hq, Nq]. */
+/* Workspace bytes fa_bwd needs: task-pool counters (256 bytes) and fp32 partial sums of dQ
+ * (B * Hq * ceil(Nq / 64) blocks of 64 x d) at the start, then D = rowsum(dO * O) fp32
+ * [B, Hq, Nq]. The first 256 + 256 * d * B * Hq * ceil(Nq / 64) bytes must be zero before a
+ * workspace's first use (allocate it zero-filled once); every call leaves them zero again, so
+ * calls with the same B, Hq, Nq and d reuse a workspace without clearing (the layout moves
+ * with them: zero it again before a call with other values), and calls that share one must not
+ * overlap. D needs no initial contents. */
 size_t fa_bwd_workspace_size(int B, int Hq, int Nq, int d);
 
 /*
@@ -71,12 +77,27 @@ size_t fa_bwd_workspace_size(int B, int Hq, int Nq, int d);
  * P = exp(scale*S - L) is recomputed per tile; dV = P^T dO; dP = dO V^T; dS = P * (dP - D) with
  * D = rowsum(dO * O); dQ = scale * dS K; dK = scale * dS^T Q. For GQA, dK and dV sum over the
  * query heads of a group. dtype FA_BF16 only (fp32 gives FA_ERR_UNSUPPORTED). dq has Q's layout,
- * dk and dv K's. dK/dV come from a key-block-outer kernel and dQ from a query-block-outer one
- * (both recompute P), so no atomics are involved and results are reproducible run to run.
+ * dk and dv K's. A key-block-outer kernel forms dK and dV and a query-block-outer kernel dQ
+ * (both recompute P); no atomics are involved, so results are reproducible run to run.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
            void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
            float scale, int dtype, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * The same backward in one key-block-outer pass that forms all five products (dQ is not
+ * recomputed): each 64-row block's dQ is summed in fp32 in the workspace by the key blocks in a
+ * fixed order, shortest task first with the causal mask, each partial sum tagged with its adder
+ * count ("Flash Attention 3/4 笔记" (KaiSpace), deterministic backward; dQ accumulated over key
+ * blocks as in Lecture 21 notes §2.6, exercise 6). Results are reproducible run to run and agree
+ * with fa_bwd up to rounding. Arguments, workspace and its contract as for fa_bwd. Supported:
+ * dtype FA_BF16, d = 128, and Nk <= 2048 without the causal mask (a head's 16 key-block
+ * workgroups must run at the same time) or Nk <= 32640 with it; other shapes return
+ * FA_ERR_UNSUPPORTED before any device work.
+ */
+int fa_bwd_single_pass(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                       const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                       int causal, float scale, int dtype, void* workspace, size_t ws_bytes, void* stream);
 
 /* ---- dropout on the probabilities (Lecture 21 notes §2.8, exercise 4) ----
  * O = (P * Z / (1 - p)) V with P the normalised probabilities; lse is still the logsumexp of the
@@ -98,8 +119,9 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
 /* Workspace bytes fa_decode needs: arrival counters of the split sequences (ceil256(4 * B * Hq)
  * bytes at the start), then fp32 partials (o, m, l) for up to 2048 + B splits of every query
  * head. The counters must be zero before a workspace's first use (allocate it zero-filled once);
- * every call leaves them zero again, so a workspace is reused without clearing. The rest of the
- * workspace needs no initial contents. */
+ * every call leaves them zero again, so calls with the same B and Hq reuse a workspace without
+ * clearing (the layout moves with them: zero it again before a call with other values). The rest
+ * of the workspace needs no initial contents. */
 size_t fa_decode_workspace_size(int B, int Hq, int Nk_max, int d);
 
 /*

@@ -69,6 +69,31 @@ def bwd(ws=P, ws_bytes=None, **kw):
                            a["dtype"], ws, ws_bytes, None)
 
 
+def bwd_single(ws=P, ws_bytes=None, **kw):
+    a = dict(B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=128, causal=0, scale=0.125, dtype=1)
+    a.update(kw)
+    need = fa.fa_bwd_workspace_size(a["B"], a["Hq"], a["Nq"], a["d"])
+    ws_bytes = need if ws_bytes is None else ws_bytes
+    return fa.lib().fa_bwd_single_pass(P, P, P, P, P, P, P, P, P, a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"],
+                                       a["causal"], a["scale"], a["dtype"], ws, ws_bytes, None)
+
+
+def test_bwd_single_pass_validation():
+    # shapes the single pass does not take are refused before any device work
+    assert bwd_single(d=64) == UNSUPPORTED
+    assert bwd_single(dtype=0) == UNSUPPORTED
+    assert bwd_single(Nk=2049) == UNSUPPORTED               # 17 key blocks without the mask
+    assert bwd_single(Nq=32641, Nk=32641, causal=1, Hq=1) == UNSUPPORTED  # 256 key blocks with it
+    assert bwd_single(ws=None) == WORKSPACE
+    assert bwd_single(ws_bytes=fa.fa_bwd_workspace_size(1, 2, 8, 128) - 1) == WORKSPACE
+    assert bwd_single(Hq=3, Hkv=2) == INVALID
+    # the workspace: 256 bytes of pool counters, the fp32 partial sums (64 rows x d per query head
+    # and 64-row block), then D padded to 256 bytes
+    pad = lambda n: -(-n // 256) * 256
+    for (B, Hq, Nq, d) in ((1, 2, 8, 128), (16, 16, 2048, 128), (2, 3, 100, 64)):
+        assert fa.fa_bwd_workspace_size(B, Hq, Nq, d) == 256 + 4 * 64 * d * B * Hq * -(-Nq // 64) + pad(4 * B * Hq * Nq)
+
+
 def test_bwd_validation():
     need = fa.fa_bwd_workspace_size(1, 2, 8, 64)
     assert need >= 2 * 8 * 4  # D = rowsum(dO * O), fp32 per (head, row)

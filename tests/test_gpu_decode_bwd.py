@@ -104,19 +104,40 @@ def test_decode_config():
     check("L", lse, rl, "bf16", is_lse=True)
 
 
-def run_fwd_bwd(inp, causal, scale):
+def bwd_zeroed_bytes(B, Hq, Nq, d):
+    """Bytes at the start of the fa_bwd workspace that are zero between calls: the task-pool
+    counters and the tagged fp32 partial sums of dQ."""
+    return 256 + 4 * 64 * d * B * Hq * -(-Nq // 64)
+
+
+def run_fwd_bwd(inp, causal, scale, ws=None, single_pass=False):
     import torch
 
     fa = _fa()
+    bwd = fa.fa_bwd_single_pass if single_pass else fa.fa_bwd
     q, k, v, do = (to_dev(inp[n], "bf16") for n in ("q", "k", "v", "do"))
     o, lse = fa.forward(q, k, v, causal=causal, scale=scale)
     B, Nq, Hq, d = q.shape
-    # workspace bytes all 0xFF (NaN as fp32): a row of D the kernels never wrote would show
-    ws = torch.full((fa.fa_bwd_workspace_size(B, Hq, Nq, d),), 255, dtype=torch.uint8, device="cuda")
+    nc = bwd_zeroed_bytes(B, Hq, Nq, d)
+    if ws is None:
+        # D all 0xFF (NaN as fp32): a row of D the kernels read before writing would show; the
+        # counters and partial sums start at zero, as the contract asks
+        ws = torch.full((fa.fa_bwd_workspace_size(B, Hq, Nq, d),), 255, dtype=torch.uint8, device="cuda")
+        ws[:nc] = 0
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, causal, scale)
+    bwd(q, k, v, o, do, lse, dq, dk, dv, ws, causal, scale)
     torch.cuda.synchronize()
+    # every call leaves the counters and partial sums zero (a bounded wait that ran out would
+    # leave its count here)
+    assert int(torch.count_nonzero(ws[:nc])) == 0
     return to_np(dq), to_np(dk), to_np(dv)
+
+
+def single_pass_supported(Nk, d, causal):
+    """Shapes fa_bwd_single_pass takes: d = 128 and at most 16 key blocks of 128 without the mask
+    (the workgroups of a head run together) or 255 with it (8-bit adder tags)."""
+    n_tc = -(-Nk // 128)
+    return d == 128 and n_tc <= (255 if causal else 16)
 
 
 @pytest.mark.parametrize(
@@ -134,26 +155,37 @@ def run_fwd_bwd(inp, causal, scale):
         (1, 100, 333, 2, 1, 128, False, None),  # N_q != N_k, both ragged
         (1, 520, 70, 2, 1, 64, False, None),    # more query rows than keys
         (1, 1, 1, 1, 1, 128, False, None),      # one query, one key: dS = 0, dV = dO
+        (1, 256, 2048, 4, 2, 128, False, None),  # 16 key blocks, fewer query blocks than key blocks
+        (1, 64, 2100, 2, 1, 128, False, None),  # 17 key blocks without the mask: the two-kernel path
+        (1, 1100, 1100, 2, 1, 128, True, None),  # causal GQA, 9 key blocks, ragged
     ],
 )
-def test_bwd_small(B, Nq, Nk, Hq, Hkv, d, causal, seed):
+@pytest.mark.parametrize("single_pass", [False, True])
+def test_bwd_small(B, Nq, Nk, Hq, Hkv, d, causal, seed, single_pass):
     if seed is None:
         seed = 900 + Nq + d if Nq == Nk else 950 + Nq + 3 * Nk + d
-    say(f"bwd B={B} Nq={Nq} Nk={Nk} Hq={Hq} Hkv={Hkv} d={d} causal={causal} seed={seed}")
+    say(f"bwd B={B} Nq={Nq} Nk={Nk} Hq={Hq} Hkv={Hkv} d={d} causal={causal} seed={seed} single_pass={single_pass}")
     inp = workloads.make_attention_inputs(B, Nq, Nk, Hq, Hkv, d, seed=seed, with_do=True)
     scale = 1.0 / math.sqrt(d)
-    dq, dk, dv = run_fwd_bwd(inp, causal, scale)
+    if single_pass and not single_pass_supported(Nk, d, causal):
+        fa = _fa()
+        with pytest.raises(fa.FAError) as e:
+            run_fwd_bwd(inp, causal, scale, single_pass=True)
+        assert e.value.code == -2  # FA_ERR_UNSUPPORTED, before any device work
+        return
+    dq, dk, dv = run_fwd_bwd(inp, causal, scale, single_pass=single_pass)
     rq, rk, rv = ora.backward(inp["q"], inp["k"], inp["v"], inp["do"], causal, scale)
     check("dQ", dq, rq, "bf16")
     check("dK", dk, rk, "bf16")
     check("dV", dv, rv, "bf16")
 
 
-def test_bwd_config():
+@pytest.mark.parametrize("single_pass", [False, True])
+def test_bwd_config(single_pass):
     w = workloads.WORKLOADS["bwd_bf16_causal_b8h16n4096d128"]
-    say(f"bwd config {w.name}")
+    say(f"bwd config {w.name} single_pass={single_pass}")
     inp = workloads.make_workload_inputs(w)
-    dq, dk, dv = run_fwd_bwd(inp, True, w.scale)
+    dq, dk, dv = run_fwd_bwd(inp, True, w.scale, single_pass=single_pass)
     pairs = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
     sel = [pairs[i] for i in workloads.sample_indices(len(pairs), 3, 51)]
     say(f"  oracle gradients on heads {sel}")
@@ -164,13 +196,14 @@ def test_bwd_config():
         check(f"dV[b={b},h={g}]", dv[b, :, g], rv[b, :, g], "bf16", config=True)
 
 
+@pytest.mark.parametrize("single_pass", [False, True])
 @pytest.mark.parametrize("causal", [False, True])
-def test_bwd_training_shape(causal):
+def test_bwd_training_shape(causal, single_pass):
     # the shape and launch configuration the benchmark step times, on sampled heads
     w = workloads.WORKLOADS["fwd_bf16_b16h16n2048d128"]
-    say(f"bwd training shape {w.name} causal={causal}")
+    say(f"bwd training shape {w.name} causal={causal} single_pass={single_pass}")
     inp = workloads.make_attention_inputs(w.B, w.Nq, w.Nk, w.Hq, w.Hkv, w.d, seed=w.seed, with_do=True)
-    dq, dk, dv = run_fwd_bwd(inp, causal, w.scale)
+    dq, dk, dv = run_fwd_bwd(inp, causal, w.scale, single_pass=single_pass)
     pairs = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
     sel = [pairs[i] for i in workloads.sample_indices(len(pairs), 3, 61 + causal)]
     say(f"  oracle gradients on heads {sel}")
@@ -181,17 +214,39 @@ def test_bwd_training_shape(causal):
         check(f"dV[b={b},h={g}]", dv[b, :, g], rv[b, :, g], "bf16", config=True)
 
 
-def test_bwd_and_fwd_are_reproducible():
+@pytest.mark.parametrize("single_pass", [False, True])
+def test_bwd_reuses_its_workspace(single_pass):
+    # three calls on one workspace (same B, Hq, Nq; other kv heads, mask and inputs): the counters
+    # and partial sums each call leaves must be the zeros the next one starts from, and the
+    # results match a call on a fresh workspace bit for bit
+    import torch
+
+    fa = _fa()
+    ws = torch.zeros(fa.fa_bwd_workspace_size(2, 4, 700, 128), dtype=torch.uint8, device="cuda")
+    for (Hkv, causal, seed) in ((2, True, 77), (4, False, 78), (1, True, 79)):
+        say(f"bwd workspace reuse B=2 N=700 Hq=4 Hkv={Hkv} causal={causal} single_pass={single_pass}")
+        inp = workloads.make_attention_inputs(2, 700, 700, 4, Hkv, 128, seed=seed, with_do=True)
+        got = run_fwd_bwd(inp, causal, 0.09, ws=ws, single_pass=single_pass)
+        ref = run_fwd_bwd(inp, causal, 0.09, single_pass=single_pass)
+        for a, b in zip(got, ref):
+            assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("single_pass", [False, True])
+def test_bwd_and_fwd_are_reproducible(single_pass):
     # no atomics and a fixed summation order: two calls give bit-identical results
     import torch
 
     fa = _fa()
     inp = workloads.make_attention_inputs(2, 700, 700, 4, 2, 128, seed=4242, with_do=True)
     q, k, v, do = (to_dev(inp[n], "bf16") for n in ("q", "k", "v", "do"))
+    B, Nq, Hq, d = q.shape
     runs = []
     for _ in range(2):
         o, lse = fa.forward(q, k, v, causal=True, scale=0.1)
-        dq, dk, dv = fa.backward(q, k, v, o, do, lse, causal=True, scale=0.1)
+        ws = torch.zeros(fa.fa_bwd_workspace_size(B, Hq, Nq, d), dtype=torch.uint8, device="cuda")
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        (fa.fa_bwd_single_pass if single_pass else fa.fa_bwd)(q, k, v, o, do, lse, dq, dk, dv, ws, True, 0.1)
         torch.cuda.synchronize()
         runs.append([t.clone() for t in (o, lse, dq, dk, dv)])
     for a, b in zip(*runs):
