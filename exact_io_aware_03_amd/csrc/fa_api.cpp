@@ -138,7 +138,6 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v, const float* q_sca
     if (!aligned16(p)) return FA_ERR_INVALID_ARG;
   int st = common_checks(B, Hq, Hkv, Nq, Nk, d, scale);
   if (st != FA_OK) return st;
-  if (d != 128) return FA_ERR_UNSUPPORTED;
   if (causal && Nq != Nk) return FA_ERR_UNSUPPORTED;
   // buffer-resource offsets are 32-bit: one batch of O (bf16) or V (bf16) must stay below 2 GiB
   if ((long)Nq * Hq * d * 2 >= (1L << 31) || (long)Nk * Hkv * d * 2 >= (1L << 31)) return FA_ERR_UNSUPPORTED;

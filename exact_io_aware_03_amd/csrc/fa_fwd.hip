@@ -69,7 +69,10 @@ struct Tile {
   static constexpr int KROW = D * KE;                // bytes per K row
   static constexpr int ROW = D * 2;                  // bytes per V row
   static constexpr int KCH = KROW / 16, VCH = ROW / 16;  // 16-byte chunks per row
-  static constexpr int K_BYTES = BC * KROW;
+  // K area: the tile, padded to one 16-byte load per wave (an E4M3 tile at d=64 is 4 KiB; the
+  // upper waves' loads then fetch nothing and fill the padding with zeros)
+  static constexpr int K_BYTES = (BC * KROW < kWaves * 1024) ? kWaves * 1024 : BC * KROW;
+  static constexpr int K_ROWS_LDS = K_BYTES / KROW;  // rows the K loads cover (>= BC)
   static constexpr int BUF = K_BYTES + BC * ROW;     // K tile then V tile
   static constexpr int KRR = 1024 / KROW, VRR = 1024 / ROW;  // rows one wave-wide 16-byte DMA covers
   static constexpr int KDMA = K_BYTES / 1024 / kWaves;  // DMA instructions per wave per tile (K)
@@ -95,8 +98,12 @@ template <int D>
 __device__ __forceinline__ int k_swz(int row) {
   return D == 128 ? (row & 15) : ((row >> 1) & 7);
 }
-// The same for an E4M3 K tile at d=128 (128-byte rows, two per bank line): bits 1-3.
-__device__ __forceinline__ int k8_swz(int row) { return (row >> 1) & 7; }
+// The same for an E4M3 K tile: 128-byte rows at d=128 (two per bank line: bits 1-3) and 64-byte
+// rows at d=64 (four per bank line, four chunks per row: bits 2-3).
+template <int D>
+__device__ __forceinline__ int k8_swz(int row) {
+  return D == 128 ? (row >> 1) & 7 : (row >> 2) & 3;
+}
 
 // Per-lane global byte offsets of the direct-to-LDS loads of one tile: the instruction p of
 // wave w fills 1 KiB of LDS (region kWaves*p+w), lane i landing on row RR*region + i/KCH,
@@ -112,8 +119,9 @@ struct TileDma {
     for (int p = 0; p < T::KDMA; ++p) {
       const int row = T::KRR * (kWaves * p + w) + lane / T::KCH;
       const int pc = lane % T::KCH;
-      const int sw = F8 ? k8_swz(row) : k_swz<D>(row);
-      k_off[p] = (int)(row * k_row * T::KE + (pc ^ sw) * 16);
+      const int sw = F8 ? k8_swz<D>(row) : k_swz<D>(row);
+      // rows of the padding: an offset past any buffer range (zeros, no memory access)
+      k_off[p] = row < BC ? (int)(row * k_row * T::KE + (pc ^ sw) * 16) : 0x7ffffff0;
     }
 #pragma unroll
     for (int p = 0; p < T::VDMA; ++p) {
@@ -215,7 +223,7 @@ __device__ __forceinline__ void scores_f8(const char* kt, int krow0, int h, cons
   for (int kb = 0; kb < 2; ++kb) {
     const int row = 32 * kb + krow0;
     const char* kr = kt + row * D;
-    const int sw = k8_swz(row);
+    const int sw = k8_swz<D>(row);
 #pragma unroll
     for (int qh = 0; qh < QH; ++qh) zero16(s[qh][kb]);
 #pragma unroll
@@ -713,10 +721,14 @@ hipError_t launch_fwd_dropout(const FwdArgs& a, int d, hipStream_t s) {
 }
 
 hipError_t launch_fwd_fp8(const FwdArgs& a, int d, hipStream_t s) {
-  if (d != 128) return hipErrorInvalidValue;
   const dim3 grid(a.n_tasks), block(kThreads);
-  if (a.causal) hipLaunchKernelGGL((fwd_fp8_kernel<128, true>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((fwd_fp8_kernel<128, false>), grid, block, 0, s, a);
+  if (d == 128) {
+    if (a.causal) hipLaunchKernelGGL((fwd_fp8_kernel<128, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((fwd_fp8_kernel<128, false>), grid, block, 0, s, a);
+  } else {
+    if (a.causal) hipLaunchKernelGGL((fwd_fp8_kernel<64, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((fwd_fp8_kernel<64, false>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 

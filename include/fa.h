@@ -176,7 +176,7 @@ int fa_quantize_fp8(const void* x, const float* signs, void* x8, float* scales, 
 
 /* Forward from E4M3 q8 [B,Nq,Hq,d] and k8 [B,Nk,Hkv,d] with their block scales (as written by
  * fa_quantize_fp8) and bf16 v [B,Nk,Hkv,d]: the fa_fwd result for Q = decode(q8) * q_scale and
- * K = decode(k8) * k_scale. d must be 128. o bf16 [B,Nq,Hq,d], lse fp32 [B,Hq,Nq]. */
+ * K = decode(k8) * k_scale. d in {64, 128}. o bf16 [B,Nq,Hq,d], lse fp32 [B,Hq,Nq]. */
 int fa_fwd_fp8(const void* q8, const void* k8, const void* v, const float* q_scale, const float* k_scale,
                void* o, float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                void* stream);

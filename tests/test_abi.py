@@ -234,7 +234,7 @@ def test_fp8_validation_and_scale_count():
         return L.fa_fwd_fp8(a["q8"], a["k8"], a["v"], a["qs"], a["ks"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
                             a["Nq"], a["Nk"], a["d"], a["causal"], a["scale"], None)
     assert f(qs=None) == INVALID and f(ks=None) == INVALID and f(k8=None) == INVALID
-    assert f(d=64) == UNSUPPORTED  # the FP8 forward is built for d = 128
+    assert f(d=96) == UNSUPPORTED  # d in {64, 128}
     assert f(causal=1, Nk=9) == UNSUPPORTED and f(Hq=3, Hkv=2) == INVALID and f(scale=0.0) == INVALID
 
 

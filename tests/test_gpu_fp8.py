@@ -69,17 +69,21 @@ def run_fwd_fp8(q8, qs, k8, ks, v, causal, scale):
     return to_np(o), to_np(lse)
 
 
-@pytest.mark.parametrize("B,Nq,Nk,Hq,Hkv,causal", [
-    (1, 256, 256, 1, 1, False),
-    (1, 256, 256, 1, 1, True),
-    (2, 300, 300, 4, 2, True),   # ragged, GQA
-    (1, 77, 333, 4, 1, False),   # N_q != N_k
-    (1, 1, 1, 1, 1, False),
+@pytest.mark.parametrize("B,Nq,Nk,Hq,Hkv,causal,d", [
+    (1, 256, 256, 1, 1, False, 128),
+    (1, 256, 256, 1, 1, True, 128),
+    (2, 300, 300, 4, 2, True, 128),   # ragged, GQA
+    (1, 77, 333, 4, 1, False, 128),   # N_q != N_k
+    (1, 1, 1, 1, 1, False, 128),
+    # d = 64: 64-byte E4M3 rows, the K tile padded to one load per wave
+    (1, 256, 256, 2, 1, False, 64),
+    (2, 300, 300, 4, 2, True, 64),    # ragged, GQA
+    (1, 77, 333, 4, 1, False, 64),
+    (1, 1, 1, 1, 1, False, 64),
 ])
-def test_fwd_fp8_small(B, Nq, Nk, Hq, Hkv, causal):
-    d = 128
-    say(f"fwd fp8 B={B} Nq={Nq} Nk={Nk} Hq={Hq} Hkv={Hkv} causal={causal}")
-    inp = workloads.make_attention_inputs(B, Nq, Nk, Hq, Hkv, d, seed=1500 + Nq + Nk)
+def test_fwd_fp8_small(B, Nq, Nk, Hq, Hkv, causal, d):
+    say(f"fwd fp8 B={B} Nq={Nq} Nk={Nk} Hq={Hq} Hkv={Hkv} causal={causal} d={d}")
+    inp = workloads.make_attention_inputs(B, Nq, Nk, Hq, Hkv, d, seed=1500 + Nq + Nk + (0 if d == 128 else 64))
     signs = _signs(d, 8)
     q8, qs, qd = ofp8.quantize(inp["q"], signs)
     k8, ks, kd = ofp8.quantize(inp["k"], signs)
