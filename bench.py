@@ -455,6 +455,19 @@ def extra_parts(fa, w, ff, bf, results, reps):
     del q, k, v, do, o, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
 
+    # the forward with a quarter of the exponentials from the FMA-unit polynomial (training shape)
+    log("[bench] fwd_poly_exp2_b16h16n2048d128")
+    inp = workloads.make_attention_inputs(w.B, w.Nq, w.Nk, w.Hq, w.Hkv, w.d, w.seed, w.dtype)
+    q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+    del inp
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda")
+    for m in (False, True):
+        t = time_launches(lambda: fa.fa_fwd_poly_exp2(q, k, v, o, lse, causal=m, scale=w.scale), reps)
+        results[f"fwd_poly_exp2_{'causal' if m else 'nc'}_b16h16n2048d128"] = rate_entry(t, ff[m], "bf16")
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+
     # FP8 forward on the training shape: Q and K quantised to E4M3 beforehand (as the kernel
     # producing them would hand them over), so the timed call is the attention alone; the
     # quantise pass is timed on its own (HBM bound: 2 bytes read, 1 written per value)

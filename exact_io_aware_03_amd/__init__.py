@@ -28,7 +28,8 @@ EXPORTED = (
     "fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_workspace_size", "fa_strerror",
     "fa_version", "fa_wave_efficiency", "fa_plan_splits", "fa_schedule_makespan", "fa_causal_tiles",
     "fa_fp8_scale_count", "fa_quantize_fp8", "fa_fwd_fp8", "fa_fwd_dropout", "fa_bwd_dropout",
-    "fa_lpt_makespan", "fa_build_info", "fa_decode_noalloc", "fa_bwd_single_pass",
+    "fa_lpt_makespan", "fa_build_info", "fa_decode_noalloc", "fa_bwd_single_pass", "fa_fwd_poly_exp2",
+    "fa_exp2_poly",
 )
 
 _lib = None
@@ -57,6 +58,10 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd.restype = i
     L.fa_bwd_single_pass.argtypes = [vp] * 9 + [i] * 7 + [f, i, vp, sz, vp]
     L.fa_bwd_single_pass.restype = i
+    L.fa_fwd_poly_exp2.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+    L.fa_fwd_poly_exp2.restype = i
+    L.fa_exp2_poly.argtypes = [vp, vp, ctypes.c_long, vp]
+    L.fa_exp2_poly.restype = i
     L.fa_decode_workspace_size.argtypes = [i, i, i, i]
     L.fa_decode_workspace_size.restype = sz
     L.fa_decode.argtypes = [vp] * 6 + [i] * 6 + [f, i, vp, sz, vp]
@@ -135,6 +140,24 @@ def fa_fwd(q, k, v, o, lse, causal: bool = False, scale: float | None = None, st
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     _check(lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, int(causal),
                         scale, _dtype_code(q), _stream(stream)))
+
+
+def fa_fwd_poly_exp2(q, k, v, o, lse, causal: bool = False, scale: float | None = None, stream=None) -> None:
+    """fa_fwd (bf16) with a quarter of the exponentials from the FMA-unit polynomial."""
+    _need_contig(q, k, v, o, lse)
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    _check(lib().fa_fwd_poly_exp2(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, int(causal),
+                                  scale, _stream(stream)))
+
+
+def fa_exp2_poly(x, y, stream=None) -> None:
+    """y = 2^x from the FMA-unit polynomial, fp32 device tensors of equal size."""
+    _need_contig(x, y)
+    if x.numel() != y.numel():
+        raise ValueError("x and y differ in size")
+    _check(lib().fa_exp2_poly(_ptr(x), _ptr(y), x.numel(), _stream(stream)))
 
 
 def _bwd_call(fn, q, k, v, o, dout, lse, dq, dk, dv, workspace, causal, scale, stream) -> None:

@@ -72,7 +72,7 @@ const char* fa_strerror(int code) {
 
 static int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
                       int Nq, int Nk, int d, int causal, float scale, int dtype, const fa::Dropout* drop,
-                      void* stream) {
+                      void* stream, bool poly = false) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_INVALID_ARG;
   int st = common_checks(B, Hq, Hkv, Nq, Nk, d, scale);
@@ -95,6 +95,7 @@ static int fwd_common(const void* q, const void* k, const void* v, void* o, floa
   if (tasks > INT_MAX) return FA_ERR_INVALID_ARG;
   a.n_tasks = (int)tasks;
   hipStream_t s = (hipStream_t)stream;
+  if (poly) return hip_status(fa::launch_fwd_poly(a, d, s));
   if (drop && drop->t > 0) {
     a.drop = *drop;
     return hip_status(fa::launch_fwd_dropout(a, d, s));
@@ -105,6 +106,17 @@ static int fwd_common(const void* q, const void* k, const void* v, void* o, floa
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Nq,
            int Nk, int d, int causal, float scale, int dtype, void* stream) {
   return fwd_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, dtype, nullptr, stream);
+}
+
+int fa_fwd_poly_exp2(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                     int Nq, int Nk, int d, int causal, float scale, void* stream) {
+  return fwd_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, FA_BF16, nullptr, stream, true);
+}
+
+int fa_exp2_poly(const float* x, float* y, long n, void* stream) {
+  if (n < 0 || (n > 0 && (!x || !y))) return FA_ERR_INVALID_ARG;
+  if (n == 0) return FA_OK;
+  return hip_status(fa::launch_exp2_poly(x, y, n, (hipStream_t)stream));
 }
 
 int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Nq,

@@ -103,6 +103,19 @@ __device__ __forceinline__ void zero16(f32x16& x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 2^x on the FMA units (Lecture 21 notes §5.2): 2^x = 2^floor(x) * 2^f, f = x - floor(x) in
+// [0, 1); 2^f from the cubic 1 + c1 f + c2 f^2 + c3 f^3 (p(0) = 1, minimax relative error
+// 8.6e-5 on [0, 1), fitted with Lawson's algorithm by exact_io_aware_03_amd/fit_exp2.py), and
+// floor(x) added to the float's exponent field. Arguments below -127 (masked scores are -inf)
+// give exactly 0.
+__device__ __forceinline__ float exp2_poly(float x) {
+  x = fmaxf(x, -127.f);
+  const float fl = floorf(x);
+  const float f = x - fl;
+  const float p = fmaf(fmaf(fmaf(7.706772536e-02f, f, 2.276442498e-01f), f, 6.951169372e-01f), f, 1.f);
+  return __int_as_float(__float_as_int(p) + ((int)fl << 23));
+}
+
 // Hardware dispatches consecutive workgroup ids round-robin over the 8 XCDs. Give every XCD
 // one contiguous range of the task list instead, so tasks that read the same K/V rows run
 // under the same L2. Bijective for any n.

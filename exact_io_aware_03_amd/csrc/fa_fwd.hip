@@ -296,7 +296,7 @@ __device__ __forceinline__ bf16x8 v_frag(const char* vt, int ks, int db, int lan
 // of tile j; with NEXT, the scores of tile j+1 are produced into s on exit.
 // c: scale * log2(e) (times this wave's Q block scale on the FP8 path); kscale: the FP8 path's
 // per-tile K block scales.
-template <int D, bool CAUSAL, bool NEXT, bool F8, bool DROP>
+template <int D, bool CAUSAL, bool NEXT, bool F8, bool DROP, bool POLY = false>
 __device__ __forceinline__ void tile_step(char* smem, int j, const char* kp, const char* vp, long k_row, int nk_load,
                                           int nk, const TileDma<D, F8>& dm, int q0, int l32, int h, int lane,
                                           int krow0, float c_in, cfloat* kscale, const Dropout& dp, int bh,
@@ -347,7 +347,11 @@ __device__ __forceinline__ void tile_step(char* smem, int j, const char* kp, con
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[qh][kb][i] = fast_exp2(fmaf(s[qh][kb][i], c, -m_use[qh]));
+      for (int i = 0; i < 16; ++i) {
+        const float x = fmaf(s[qh][kb][i], c, -m_use[qh]);
+        // POLY: a quarter of the exponentials (FA4 takes 10-25% per row) on the FMA units
+        s[qh][kb][i] = (POLY && i % 4 == 0) ? exp2_poly(x) : fast_exp2(x);
+      }
   // ---- phase B: O^T += V^T P^T (MFMA) interleaved with packing and the row sums (VALU) ----
   // dropout (§2.8): keep[qh] bit 8ks + x is key kv0 + 16ks + 8h + x of this lane's row.
   // Without the mask the bits are made one tile ahead: the next tile's here, while the P V
@@ -405,7 +409,7 @@ __device__ __forceinline__ void tile_step(char* smem, int j, const char* kp, con
   wait_vm_barrier<T::VMCNT>();  // tile j+2 landed; tile j+3 may still be in flight
 }
 
-template <int D, bool CAUSAL, bool F8, bool DROP>
+template <int D, bool CAUSAL, bool F8, bool DROP, bool POLY = false>
 __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   using T = Tile<D, F8>;
 
@@ -513,7 +517,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   int j = 0;
   if constexpr (!CAUSAL) {
     if (last_w & 1) {
-      tile_step<D, CAUSAL, true, F8, DROP>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, a.drop, bh, qf, s0, s1,
+      tile_step<D, CAUSAL, true, F8, DROP, POLY>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, a.drop, bh, qf, s0, s1,
                                  o, m, l, keep);
 #pragma unroll
       for (int qh = 0; qh < QH; ++qh) {
@@ -524,19 +528,19 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
     }
   }
   for (; j + 1 < last_w; j += 2) {
-    tile_step<D, CAUSAL, true, F8, DROP>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, a.drop, bh, qf, s0, s1,
+    tile_step<D, CAUSAL, true, F8, DROP, POLY>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, a.drop, bh, qf, s0, s1,
                                o, m, l, keep);
-    tile_step<D, CAUSAL, true, F8, DROP>(smem, j + 1, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, a.drop, bh, qf, s1,
+    tile_step<D, CAUSAL, true, F8, DROP, POLY>(smem, j + 1, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, a.drop, bh, qf, s1,
                                s0, o, m, l, keep);
   }
   if (CAUSAL && j < last_w) {
-    tile_step<D, CAUSAL, true, F8, DROP>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, a.drop, bh, qf, s0, s1,
+    tile_step<D, CAUSAL, true, F8, DROP, POLY>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, a.drop, bh, qf, s0, s1,
                                o, m, l, keep);
     ++j;
-    tile_step<D, CAUSAL, false, F8, DROP>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, a.drop, bh, qf, s1,
+    tile_step<D, CAUSAL, false, F8, DROP, POLY>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, a.drop, bh, qf, s1,
                                 s0, o, m, l, keep);
   } else {
-    tile_step<D, CAUSAL, false, F8, DROP>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, a.drop, bh, qf, s0,
+    tile_step<D, CAUSAL, false, F8, DROP, POLY>(smem, j, kp, vp, a.k_row, nk_load, a.Nk, dm, q0, l32, h, lane, krow0, cw, ksc, a.drop, bh, qf, s0,
                                 s1, o, m, l, keep);
   }
   ++j;
@@ -584,6 +588,22 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void fwd_drop_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[NBUF * Tile<D>::BUF];
   fwd_body<D, CAUSAL, false, true>(a, smem);
+}
+
+// Forward with a quarter of the exponentials from exp2_poly (Lecture 21 notes §5.2). On gfx950
+// the exponential is a VALU instruction rather than a separate narrow unit, so the polynomial
+// costs more issue time than the v_exp_f32 it replaces; the variant is kept to measure that and
+// to pin the polynomial's accuracy inside attention.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void fwd_poly_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[NBUF * Tile<D>::BUF];
+  fwd_body<D, CAUSAL, false, false, true>(a, smem);
+}
+
+// y = exp2_poly(x), elementwise (for the accuracy checks of the polynomial).
+__global__ __launch_bounds__(256) void exp2_poly_kernel(const float* x, float* y, long n) {
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x)
+    y[i] = exp2_poly(x[i]);
 }
 
 template <int D, bool CAUSAL>
@@ -729,6 +749,24 @@ hipError_t launch_fwd_fp8(const FwdArgs& a, int d, hipStream_t s) {
     if (a.causal) hipLaunchKernelGGL((fwd_fp8_kernel<64, true>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((fwd_fp8_kernel<64, false>), grid, block, 0, s, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_poly(const FwdArgs& a, int d, hipStream_t s) {
+  const dim3 grid(a.n_tasks), block(kThreads);
+  if (d == 128) {
+    if (a.causal) hipLaunchKernelGGL((fwd_poly_kernel<128, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((fwd_poly_kernel<128, false>), grid, block, 0, s, a);
+  } else {
+    if (a.causal) hipLaunchKernelGGL((fwd_poly_kernel<64, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((fwd_poly_kernel<64, false>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_exp2_poly(const float* x, float* y, long n, hipStream_t s) {
+  const long want = (n + 255) / 256;
+  hipLaunchKernelGGL(exp2_poly_kernel, dim3((unsigned)(want < 4096 ? (want > 0 ? want : 1) : 4096)), dim3(256), 0, s, x, y, n);
   return hipGetLastError();
 }
 

@@ -99,6 +99,8 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, hipStream_t s);
 hipError_t launch_fwd_fp8(const FwdArgs& a, int d, hipStream_t s);
 hipError_t launch_fwd_dropout(const FwdArgs& a, int d, hipStream_t s);
+hipError_t launch_fwd_poly(const FwdArgs& a, int d, hipStream_t s);
+hipError_t launch_exp2_poly(const float* x, float* y, long n, hipStream_t s);
 hipError_t launch_bwd_dropout(const BwdArgs& a, int d, hipStream_t s);
 constexpr int kFp8Block = 64;     // rows per FP8 quantisation block (one scale each)
 hipError_t launch_quantize_fp8(const void* x, const float* signs, void* x8, float* scales, int B, int N, int H,

@@ -99,6 +99,18 @@ int fa_bwd_single_pass(const void* q, const void* k, const void* v, const void* 
                        const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d,
                        int causal, float scale, int dtype, void* workspace, size_t ws_bytes, void* stream);
 
+/* ---- exponentials on the FMA units (Lecture 21 notes §5.2) ----
+ * 2^x = 2^floor(x) * p(x - floor(x)) with p(f) = 1 + c1 f + c2 f^2 + c3 f^3, p(0) = 1, a minimax
+ * fit of 2^f on [0, 1) (relative error 8.6e-5; coefficients from our own fit with Lawson's
+ * algorithm, exact_io_aware_03_amd/fit_exp2.py), the power of two added to the exponent field.
+ * fa_fwd_poly_exp2 is fa_fwd (bf16) with a quarter of the exponentials of every tile (one in
+ * four per lane) computed this way instead of with v_exp_f32, as FA4 splits them; the result
+ * agrees with fa_fwd within the bf16 rounding of P. fa_exp2_poly evaluates the same function
+ * elementwise on n fp32 device values (x and y on the device; arguments below -127 give 0). */
+int fa_fwd_poly_exp2(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                     int Nq, int Nk, int d, int causal, float scale, void* stream);
+int fa_exp2_poly(const float* x, float* y, long n, void* stream);
+
 /* ---- dropout on the probabilities (Lecture 21 notes §2.8, exercise 4) ----
  * O = (P * Z / (1 - p)) V with P the normalised probabilities; lse is still the logsumexp of the
  * scores without dropout. Only the seed is kept: the keep mask Z is regenerated wherever it is
