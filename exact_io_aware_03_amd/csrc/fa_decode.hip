@@ -70,6 +70,10 @@ __device__ __forceinline__ int seq_blocks(int n) { return (n + kUnit - 1) / kUni
 // Cache policy of the partials' loads and stores: sc1, coherent across the XCDs' L2 caches
 // (the workers that write a sequence's partials and the one that merges them may run on any).
 constexpr int kCoherent = 16;
+// Cache policy of the K/V cache loads: non-temporal. Every cache byte is read exactly once, and
+// streaming loads marked this way reach ~7.2 TB/s where plain ones stay near 6 (a read-only
+// probe over 2 GiB); the whole call went from ~212 to ~190 us.
+constexpr int kStream = 2;
 
 // Merge the partials of sequence b for the G query heads hq0 .. hq0 + G - 1, written by the
 // workers w_first .. w_last into slots (worker + b): O = sum_c 2^(m_c - M) o_c / l,
@@ -221,7 +225,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_partial_kernel(DecArgs a) {
       auto load_k = [&](int base) {
         const rsrc_t r = make_rsrc(kp + (long)base * a.k_row, ((long)(k_hi - 1 - base) * a.k_row + D) * 2);
 #pragma unroll
-        for (int i = 0; i < CH; ++i) kr[i] = __builtin_amdgcn_raw_buffer_load_b128(r, koff, i * KPI * row_b, 0);
+        for (int i = 0; i < CH; ++i) kr[i] = __builtin_amdgcn_raw_buffer_load_b128(r, koff, i * KPI * row_b, kStream);
       };
       auto stage_k = [&]() {
 #pragma unroll
@@ -235,11 +239,11 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_partial_kernel(DecArgs a) {
 #pragma unroll
         for (int s = 0; s < 16; ++s) {
           if (VE == 8) {
-            const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 4 * s * row_b, 0);
+            const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 4 * s * row_b, kStream);
 #pragma unroll
             for (int e = 0; e < VE / 2; ++e) vr[s][e] = t[e];
           } else {
-            const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 4 * s * row_b, 0);
+            const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 4 * s * row_b, kStream);
 #pragma unroll
             for (int e = 0; e < VE / 2; ++e) vr[s][e] = t[e];
           }
