@@ -265,12 +265,13 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
 }
 
 // Decode scratch layout for `workers` split workers: the arrival counters of the split
-// sequences [B * Hq] (int, room for B * Hkv; zero between calls), then the fp32 partial outputs
-// [(workers + B) * Hq, d] and partial (max, sum) pairs [(workers + B) * Hq, 2]. Returns the total
-// bytes; fills the three parts when base is given.
-static size_t decode_layout(int workers, int B, int Hq, int d, void* base, fa::DecArgs* a) {
+// sequences (int, room for B * Hq, of which B * Hkv are used; zero between calls; `counters`
+// ints when it is given, so that the region does not move with the shape), then the fp32
+// partial outputs [(workers + B) * Hq, d] and partial (max, sum) pairs [(workers + B) * Hq, 2].
+// Returns the total bytes; fills the three parts when base is given.
+static size_t decode_layout(int workers, int B, int Hq, int d, void* base, fa::DecArgs* a, int counters = 0) {
   const size_t slots = (size_t)(workers + B) * Hq;
-  const size_t c_bytes = align256((size_t)B * Hq * sizeof(int));
+  const size_t c_bytes = align256((size_t)(counters > 0 ? counters : (long)B * Hq) * sizeof(int));
   const size_t o_bytes = align256(slots * d * sizeof(float)), ml_bytes = align256(slots * 2 * sizeof(float));
   if (base && a) {
     a->arrive = (int*)base;
@@ -327,11 +328,16 @@ int fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, c
   fa::DecArgs a;
   const int st = decode_setup(q, k_cache, v_cache, seqlens_k, o, lse, B, Hq, Hkv, Nq, Nk_max, d, scale, dtype, a);
   if (st != FA_OK) return st;
-  if (decode_layout(fa::kDecNoAllocWorkers, B, Hq, d, nullptr, nullptr) > fa::kDecScratchBytes) return FA_ERR_SCRATCH;
+  // The counters keep one place in the array whatever the shape: every call leaves those it
+  // used zero, and no call's partials reach them.
+  if ((long)B * Hq > fa::kDecNoAllocCounters ||
+      decode_layout(fa::kDecNoAllocWorkers, B, Hq, d, nullptr, nullptr, fa::kDecNoAllocCounters) >
+          fa::kDecScratchBytes)
+    return FA_ERR_SCRATCH;
   void* base = nullptr;
   const hipError_t e = fa::decode_scratch(&base);
   if (e != hipSuccess) return hip_status(e);
-  decode_layout(fa::kDecNoAllocWorkers, B, Hq, d, base, &a);
+  decode_layout(fa::kDecNoAllocWorkers, B, Hq, d, base, &a, fa::kDecNoAllocCounters);
   a.max_workers = fa::kDecNoAllocWorkers;
   return hip_status(fa::launch_decode(a, (hipStream_t)stream));
 }

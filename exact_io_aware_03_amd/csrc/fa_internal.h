@@ -89,6 +89,9 @@ constexpr int kFwdF32Keys = 32;   // keys per tile in the fp32 forward
 constexpr int kDecMaxWorkers = 2048;  // decode workers (partials per sequence boundary)
 constexpr int kDecNoAllocWorkers = 256;  // worker cap of the decode that allocates nothing
 constexpr size_t kDecScratchBytes = size_t(32) << 20;  // its static per-GPU scratch array
+// Arrival counters at the start of that array: a region of fixed size, so that the counters of
+// every problem shape lie where no call writes partials.
+constexpr int kDecNoAllocCounters = 131072;
 constexpr int kBwdKeys = 128;     // keys per dK/dV workgroup (4 key slices x 32)
 constexpr int kBwdRows = 64;      // query rows per dK/dV inner step
 constexpr int kBwdDqRows = 256;   // query rows per dQ workgroup (8 waves x 32)

@@ -156,11 +156,13 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int
  * Decode for callers that cannot allocate device memory: code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc. Same arguments and result as fa_decode minus
  * the workspace. The arrival counters and split partials live in a fixed 32 MiB device array
- * inside the library (one per GPU, zero when the library loads, held until the process ends;
- * every call leaves the counters zero), and at most 256 workers share the block list. A problem
- * whose scratch, 4 * B * Hq + (256 + B) * Hq * (d + 2) * 4 bytes with each of the three parts
- * rounded up to 256 bytes, exceeds the array returns FA_ERR_SCRATCH before any HIP call. The
- * call allocates nothing. Every call on a GPU uses that GPU's one array: calls that overlap on
+ * inside the library (one per GPU, zero when the library loads, held until the process ends),
+ * and at most 256 workers share the block list. The counters occupy the first 512 KiB of the
+ * array whatever the shape, and every call leaves them zero, so calls of any shapes follow one
+ * another without clearing. A problem with B * Hq > 131072, or whose partials,
+ * (256 + B) * Hq * (d + 2) * 4 bytes with the o and (m, l) parts each rounded up to 256 bytes,
+ * do not fit in the remaining 31.5 MiB, returns FA_ERR_SCRATCH before any HIP call. The call
+ * allocates nothing. Every call on a GPU uses that GPU's one array: calls that overlap on
  * one GPU (on two streams, or from two threads) race and must be serialised by the caller.
  */
 int fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int* seqlens_k, void* o,

@@ -138,7 +138,8 @@ def dec_noalloc(**kw):
 
 def test_decode_noalloc_validation_and_scratch_limit():
     # the same argument checks as fa_decode, then the static scratch limit, all before any HIP call:
-    # 4 B Hq + (256 + B) * Hq * (d + 2) * 4 bytes must fit in 32 MiB
+    # the counters take a fixed 512 KiB at the start of the 32 MiB array, and the partials,
+    # (256 + B) * Hq * (d + 2) * 4 bytes, must fit in the rest
     assert dec_noalloc(Nq=2) == INVALID
     assert dec_noalloc(seqlens=None) == INVALID
     assert dec_noalloc(dtype=0) == UNSUPPORTED
@@ -146,6 +147,11 @@ def test_decode_noalloc_validation_and_scratch_limit():
     SCRATCH = -5
     assert dec_noalloc(B=2000, Hq=32, Hkv=8) == SCRATCH  # (2256 * 32 * 130 * 4) B > 32 MiB
     assert dec_noalloc(B=64, Hq=256, Hkv=16) == SCRATCH  # (320 * 256 * 130 * 4) B > 32 MiB
+    # partials of B = 1740, Hq = 32, d = 128 take 31.67 MiB: they would fit beside counters sized
+    # for this shape (0.21 MiB), but not beside the fixed 512 KiB counter region
+    part = lambda B: -(-(256 + B) * 32 * 128 * 4 // 256) * 256 + -(-(256 + B) * 32 * 8 // 256) * 256
+    assert part(1740) + 4 * 1740 * 32 <= 32 << 20 < part(1740) + (512 << 10)
+    assert dec_noalloc(B=1740, Hq=32, Hkv=8) == SCRATCH
     assert b"static" in fa.lib().fa_strerror(SCRATCH)
 
 

@@ -1,6 +1,8 @@
 """fa_decode_noalloc (the decode that allocates nothing: its scratch is a static per-GPU array
-in the library) through the C ABI against fa_decode with a workspace, on two calls in a row,
-the second smaller, so the second call finds the first call's contents in the array."""
+in the library) through the C ABI against fa_decode with a workspace, on calls in a row: the
+second smaller than the first, so it finds the first call's contents in the array, and a third
+larger than the second, whose arrival counters cover more of the array than the second's did
+and must still start at zero (they lie where no call writes partials)."""
 
 import math
 
@@ -36,13 +38,16 @@ def test_decode_noalloc_matches_decode_twice():
     w = workloads.WORKLOADS["decode_bf16_b64hq32hkv8d128"]
     big = workloads.make_workload_inputs(w)
     small = workloads.make_decode_inputs(3, 8, 2, 700, 128, seed=9, lengths=[1, 300, 700])
-    for name, inp, scale in (("decode workload", big, w.scale), ("small GQA 4:1", small, 1 / math.sqrt(128))):
+    medium = workloads.make_decode_inputs(16, 16, 4, 2048, 128, seed=11, len_range=(1, 2048))
+    cases = (("decode workload", big, w.scale), ("small GQA 4:1", small, 1 / math.sqrt(128)),
+             ("medium GQA 4:1, more counters than the small call", medium, 1 / math.sqrt(128)))
+    for name, inp, scale in cases:
         say(f"noalloc {name}: B={inp['q'].shape[0]} Hq={inp['q'].shape[2]} Hkv={inp['k'].shape[2]}")
         (o1, l1), (o2, l2) = _pair(fa, inp, scale)
         say(f"  identical to fa_decode: O {np.array_equal(o1, o2)}, L {np.array_equal(l1, l2)}")
         check("O noalloc vs fa_decode", o2, o1, "bf16")
         check("L noalloc vs fa_decode", l2, l1, "bf16", is_lse=True)
-        if inp["q"].shape[0] <= 8:
+        if inp["q"].shape[0] <= 16:
             ro, rl = ora.decode(inp["q"], inp["k"], inp["v"], inp["seqlens"], scale)
             check("O noalloc vs oracle", o2, ro, "bf16")
             check("L noalloc vs oracle", l2, rl, "bf16", is_lse=True)
