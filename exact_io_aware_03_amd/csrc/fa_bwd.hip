@@ -284,9 +284,10 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = (i & 7) + 16 * (i >> 3) < thr ? kNegInf : s[i];
     }
-    // dropout: keep bit 8hi + x of row qw0 + 16hi + 8h + x for this lane's key
-    uint32_t keep16 = 0xffff;
-    if constexpr (DROP) keep16 = drop_tile_rows(a.drop, (qw0 + 8 * h) >> 2, key, bhq);
+    // dropout: byte 2hi + (x >> 2) of kw[x & 3] is the random byte of row qw0 + 16hi + 8h + x
+    // for this lane's key
+    uint32_t kw[4] = {};
+    if constexpr (DROP) drop_key_words(a.drop, (qw0 + 8 * h) >> 2, key, bhq, kw);
     // P = exp(scale S - L), dS = P (dP - D); the 8 rows (i&7) are consecutive, so L and D
     // come in as 16-byte LDS reads
 #pragma unroll
@@ -294,16 +295,15 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(BwdArgs a) {
       const int lo = lb + BUF * BQ * 4 + 64 * hi;
       const f32x4 la = ld4f(lo), lbv = ld4f(lo + 16);
       const f32x4 da = ld4f(lo + 2 * BQ * 4), dbv = ld4f(lo + 2 * BQ * 4 + 16);
-      const uint32_t keep = keep16 >> (8 * hi);
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
         const int i = 8 * hi + x;
         const float lv = x < 4 ? la[x] : lbv[x - 4], dvv = x < 4 ? da[x] : dbv[x - 4];
         const float p = fast_exp2(fmaf(s[i], a.c, -lv * kLog2e));
         if constexpr (DROP) {
-          const bool z = (keep >> x) & 1;
-          s[i] = z ? p * a.drop.scale : 0.f;                   // P Z / (1 - p)
-          g[i] = p * ((z ? g[i] * a.drop.scale : 0.f) - dvv);  // dS
+          const bool z = drop_kept(a.drop, kw[x & 3], 2 * hi + (x >> 2));
+          s[i] = z ? p : 0.f;                                   // P Z; dV takes 1 / (1 - p) at the end
+          g[i] = p * fmaf(z ? g[i] : 0.f, a.drop.scale, -dvv);  // dS = P (dP Z / (1 - p) - D)
         } else {
           s[i] = p;                  // P
           g[i] = p * (g[i] - dvv);  // dS
@@ -360,6 +360,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(BwdArgs a) {
       for (int i = 0; i < 16; ++i) {
         dk[db][i] = (dk[db][i] + red[((2 * db) * 16 + i) * 64]) * a.scale;
         dv[db][i] += red[((2 * db + 1) * 16 + i) * 64];
+        if constexpr (DROP) dv[db][i] *= a.drop.scale;
       }
     wave_sync();  // the fp32 reads above come before the bf16 tiles overwrite the area
     // Row-major bf16 tiles [32 keys][D] of dK and dV in this slice's area. Registers i, i+1
@@ -1112,20 +1113,24 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[kb][i] = 32 * kb + (i & 7) + 16 * (i >> 3) >= thr ? kNegInf : s[kb][i];
     }
-    // dropout: keep bit 16kb + 8hi + x of key kv0 + 32kb + 16hi + 8h + x for row qi
-    uint32_t keep32 = 0xffffffffu;
-    if constexpr (DROP) keep32 = drop_tile_keys(a.drop, (kv0 + 8 * h) >> 2, qi, bh);
+    // dropout: byte x & 3 of kw[4kb + 2hi + (x >> 2)] is the random byte of key
+    // kv0 + 32kb + 16hi + 8h + x for row qi
+    uint32_t kw[8] = {};
+    if constexpr (DROP) drop_row_words(a.drop, (kv0 + 8 * h) >> 2, qi, bh, kw);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int hi = 0; hi < 2; ++hi) {
-        const uint32_t keep = keep32 >> (16 * kb + 8 * hi);
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
           const int i = 8 * hi + x;
           const float p = fast_exp2(fmaf(s[kb][i], a.c, -l2));
-          if constexpr (DROP) g[kb][i] = p * (((keep >> x) & 1 ? g[kb][i] * a.drop.scale : 0.f) - dd);  // dS
-          else g[kb][i] = p * (g[kb][i] - dd);                                                        // dS
+          if constexpr (DROP) {  // dS = P (dP Z / (1 - p) - D)
+            const bool z = drop_kept(a.drop, kw[4 * kb + 2 * hi + (x >> 2)], x & 3);
+            g[kb][i] = p * fmaf(z ? g[kb][i] : 0.f, a.drop.scale, -dd);
+          } else {
+            g[kb][i] = p * (g[kb][i] - dd);  // dS
+          }
         }
       }
     // ---- dQ^T += K^T dS^T: 16-key step kk takes dS registers 8(kk&1) .. +7 of block kk/2 ----

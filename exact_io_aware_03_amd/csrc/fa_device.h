@@ -179,56 +179,76 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1
 __device__ __forceinline__ u32x4 drop_block(const Dropout& dp, int kg, int rg, int bh) {
   return philox4x32_10(u32x4{(uint32_t)kg, (uint32_t)rg, (uint32_t)bh, dp.offset}, dp.k0, dp.k1);
 }
-// bit c set when byte c of x is kept
-__device__ __forceinline__ uint32_t drop_bits(const Dropout& dp, uint32_t x) {
-  return ((x & 255u) >= dp.t ? 1u : 0u) | (((x >> 8) & 255u) >= dp.t ? 2u : 0u) |
-         (((x >> 16) & 255u) >= dp.t ? 4u : 0u) | ((x >> 24) >= dp.t ? 8u : 0u);
-}
-// Value of x in lane S of this lane's quad (DPP quad_perm broadcast).
-template <int S>
-__device__ __forceinline__ uint32_t quad_bcast(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, S | (S << 2) | (S << 4) | (S << 6), 0xf, 0xf, false);
-}
-__device__ __forceinline__ uint32_t pick4(int r, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  return r == 0 ? a : r == 1 ? b : r == 2 ? c : d;
+// Value of x in lane i ^ X of this lane's quad (DPP quad_perm).
+template <int X>
+__device__ __forceinline__ uint32_t quad_xor(uint32_t x) {
+  constexpr int ctrl = (0 ^ X) | ((1 ^ X) << 2) | ((2 ^ X) << 4) | ((3 ^ X) << 6);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, ctrl, 0xf, 0xf, false);
 }
 
-// Keep bits of one lane's row for the 64 keys 4 kgb .. +63 of a tile laid out as the score
+// Whether the position whose random byte is byte i of w is kept.
+__device__ __forceinline__ bool drop_kept(const Dropout& dp, uint32_t w, int i) {
+  return ((w >> (8 * i)) & 255u) >= dp.t;
+}
+
+// 4 x 4 transpose of words across a quad (lane r = row & 3): on entry lane r holds a[k],
+// k = 0..3; on exit b[c] is lane c's a[r]. Two exchanges: with lane r ^ 1 each lane keeps
+// the words of rows of its own parity and trades the others, then with lane r ^ 2 it keeps
+// its own row and trades the other one; a final select puts the four words in lane order.
+__device__ __forceinline__ void quad_transpose(const u32x4 a, int r, uint32_t (&b)[4]) {
+  const bool odd = r & 1, hi = r & 2;
+  // rows (r & 1) + 2j: kj is this lane's word, rj lane r ^ 1's
+  const uint32_t k0 = odd ? a[1] : a[0], k1 = odd ? a[3] : a[2];
+  const uint32_t r0 = quad_xor<1>(odd ? a[0] : a[1]), r1 = quad_xor<1>(odd ? a[2] : a[3]);
+  // row r: m0 from lane r, m1 from lane r ^ 1, u0 from lane r ^ 2, u1 from lane r ^ 3
+  const uint32_t m0 = hi ? k1 : k0, m1 = hi ? r1 : r0;
+  const uint32_t u0 = quad_xor<2>(hi ? k0 : k1), u1 = quad_xor<2>(hi ? r0 : r1);
+  const uint32_t e0 = odd ? m1 : m0, e1 = odd ? m0 : m1, f0 = odd ? u1 : u0, f1 = odd ? u0 : u1;
+  b[0] = hi ? f0 : e0;
+  b[1] = hi ? f1 : e1;
+  b[2] = hi ? e0 : f0;
+  b[3] = hi ? e1 : f1;
+}
+
+// Random words of one lane's row for the 64 keys 4 kgb .. +63 of a tile laid out as the score
 // accumulators hold them (lane = query row; the four lanes of a quad are rows 4a .. 4a+3 of one
-// row group and see the same keys): bit 8m + 4g + x is key 4 (kgb + 4m + g) + x. The eight
-// Philox calls these 64 keys need are the same for the whole quad, so lane r computes calls r
-// and r + 4 and the quad shares the words through DPP broadcasts (row = 4a + r).
-__device__ __forceinline__ uint32_t drop_tile_keys(const Dropout& dp, int kgb, int row, int bh) {
+// row group and see the same keys): w[C] covers keys 4 (kgb + 4 (C >> 1) + (C & 1)) .. +3, byte
+// x for key + x. The eight Philox calls are the same for the whole quad, so lane r computes
+// calls r and r + 4 and the quad transposes their words.
+__device__ __forceinline__ void drop_row_words(const Dropout& dp, int kgb, int row, int bh, uint32_t (&w)[8]) {
   const int a = row >> 2, r = row & 3;
   const u32x4 wa = drop_block(dp, kgb + 4 * (r >> 1) + (r & 1), a, bh);      // call c = r
   const u32x4 wb = drop_block(dp, kgb + 8 + 4 * (r >> 1) + (r & 1), a, bh);  // call c = r + 4
-  uint32_t keep = 0;
-#define FA_DROP_CALL(C, W, S)                                                                       \
-  keep |= drop_bits(dp, pick4(r, quad_bcast<S>(W[0]), quad_bcast<S>(W[1]), quad_bcast<S>(W[2]),     \
-                              quad_bcast<S>(W[3])))                                                 \
-          << (4 * (C));
-  FA_DROP_CALL(0, wa, 0) FA_DROP_CALL(1, wa, 1) FA_DROP_CALL(2, wa, 2) FA_DROP_CALL(3, wa, 3)
-  FA_DROP_CALL(4, wb, 0) FA_DROP_CALL(5, wb, 1) FA_DROP_CALL(6, wb, 2) FA_DROP_CALL(7, wb, 3)
-#undef FA_DROP_CALL
-  return keep;
+  uint32_t ta[4], tb[4];
+  quad_transpose(wa, r, ta);
+  quad_transpose(wb, r, tb);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    w[c] = ta[c];
+    w[c + 4] = tb[c];
+  }
 }
 
-// Keep bits of one lane's key for the 16 rows 4 rgb + 16 hi + 4 g + x (bit 8 hi + 4 g + x), the
-// layout of the dK/dV kernel's accumulators (lane = key; a quad's lanes are keys 4m .. 4m+3 and
-// see the same rows): the four calls are the same for the quad, lane r computes call r.
-__device__ __forceinline__ uint32_t drop_tile_rows(const Dropout& dp, int rgb, int key, int bh) {
-  const int r = key & 3, sh = 8 * r;
-  const u32x4 w = drop_block(dp, key >> 2, rgb + 4 * (r >> 1) + (r & 1), bh);  // call c = r
-  uint32_t keep = 0;
-#define FA_DROP_CALL(C)                                                                              \
-  keep |= ((((quad_bcast<C>(w[0]) >> sh) & 255u) >= dp.t ? 1u : 0u) |                                \
-           (((quad_bcast<C>(w[1]) >> sh) & 255u) >= dp.t ? 2u : 0u) |                                \
-           (((quad_bcast<C>(w[2]) >> sh) & 255u) >= dp.t ? 4u : 0u) |                                \
-           (((quad_bcast<C>(w[3]) >> sh) & 255u) >= dp.t ? 8u : 0u))                                 \
-          << (4 * (C));
-  FA_DROP_CALL(0) FA_DROP_CALL(1) FA_DROP_CALL(2) FA_DROP_CALL(3)
-#undef FA_DROP_CALL
-  return keep;
+// 4 x 4 transpose of bytes across a quad: on exit byte c of lane r is byte r of lane c's x.
+// Per-lane byte selectors of v_perm (bytes 0-3 from the partner's word, 4-7 from this lane's)
+// for the exchange with lane r ^ 1 and then with lane r ^ 2.
+__device__ __forceinline__ uint32_t quad_transpose_bytes(uint32_t x, uint32_t sel1, uint32_t sel2) {
+  const uint32_t z = __builtin_amdgcn_perm(x, quad_xor<1>(x), sel1);
+  return __builtin_amdgcn_perm(z, quad_xor<2>(z), sel2);
+}
+__device__ __forceinline__ uint32_t quad_sel1(int r) { return (r & 1) ? 0x07030501u : 0x02060004u; }
+__device__ __forceinline__ uint32_t quad_sel2(int r) { return (r & 2) ? 0x07060302u : 0x01000504u; }
+
+// Random words of one lane's key for the 16 rows 4 rgb + 16 hi + 4 g + x, the layout of the
+// dK/dV kernel's accumulators (lane = key; a quad's lanes are keys 4m .. 4m+3 and see the same
+// rows): byte C = 2 hi + g of w[x] is the row's byte. The four calls are the same for the
+// quad; lane r computes call r and the quad transposes the bytes of each row's word.
+__device__ __forceinline__ void drop_key_words(const Dropout& dp, int rgb, int key, int bh, uint32_t (&w)[4]) {
+  const int r = key & 3;
+  const u32x4 c = drop_block(dp, key >> 2, rgb + 4 * (r >> 1) + (r & 1), bh);  // call r
+  const uint32_t s1 = quad_sel1(r), s2 = quad_sel2(r);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) w[k] = quad_transpose_bytes(c[k], s1, s2);
 }
 
 }  // namespace fa

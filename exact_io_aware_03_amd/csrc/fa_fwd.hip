@@ -302,7 +302,7 @@ __device__ __forceinline__ void tile_step(char* smem, int j, const char* kp, con
                                           int krow0, float c_in, cfloat* kscale, const Dropout& dp, int bh,
                                           const typename QFrag<D, F8>::type& qf, f32x16 (&s)[QH][2],
                                           f32x16 (&sn)[QH][2], f32x16 (&o)[QH][D / 32], float (&m)[QH],
-                                          float (&l)[QH], uint32_t (&keep)[QH]) {
+                                          float (&l)[QH], uint32_t (&keep)[QH][8]) {
   using T = Tile<D, F8>;
   const float c = F8 ? c_in * kscale[j] : c_in;
   const int kv0 = j * BC;
@@ -353,19 +353,19 @@ __device__ __forceinline__ void tile_step(char* smem, int j, const char* kp, con
         s[qh][kb][i] = (POLY && i % 4 == 0) ? exp2_poly(x) : fast_exp2(x);
       }
   // ---- phase B: O^T += V^T P^T (MFMA) interleaved with packing and the row sums (VALU) ----
-  // dropout (§2.8): keep[qh] bit 8ks + x is key kv0 + 16ks + 8h + x of this lane's row.
-  // Without the mask the bits are made one tile ahead: the next tile's here, while the P V
-  // MFMAs run (they do not depend on them; 16% faster). With the mask that costs spills and the
-  // bits are made for this tile, just before use.
+  // dropout (§2.8): byte x & 3 of keep[qh][2ks + (x >> 2)] is the random byte of key
+  // kv0 + 16ks + 8h + x of this lane's row. Without the mask the words are made one tile ahead:
+  // the next tile's here, while the P V MFMAs run (they do not depend on them). With the mask
+  // that costs spills and the words are made for this tile, just before use.
   constexpr bool AHEAD = !CAUSAL;
-  uint32_t keep_next[QH];
+  uint32_t keep_next[QH][8];
   if constexpr (DROP && AHEAD && NEXT) {
 #pragma unroll
-    for (int qh = 0; qh < QH; ++qh) keep_next[qh] = drop_tile_keys(dp, (kv0 + BC + 8 * h) >> 2, q0 + 32 * qh + l32, bh);
+    for (int qh = 0; qh < QH; ++qh) drop_row_words(dp, (kv0 + BC + 8 * h) >> 2, q0 + 32 * qh + l32, bh, keep_next[qh]);
   }
   if constexpr (DROP && !AHEAD) {
 #pragma unroll
-    for (int qh = 0; qh < QH; ++qh) keep[qh] = drop_tile_keys(dp, (kv0 + 8 * h) >> 2, q0 + 32 * qh + l32, bh);
+    for (int qh = 0; qh < QH; ++qh) drop_row_words(dp, (kv0 + 8 * h) >> 2, q0 + 32 * qh + l32, bh, keep[qh]);
   }
 #pragma unroll
   for (int ks = 0; ks < BC / 16; ++ks) {
@@ -377,11 +377,10 @@ __device__ __forceinline__ void tile_step(char* smem, int j, const char* kp, con
       u32x4 pw;
       if constexpr (DROP) {
         // dropout on P: this lane's 8 keys kv0 + 16ks + 8h .. +7; the row sum l keeps the
-        // undropped values
-        const uint32_t k8 = keep[qh] >> (8 * ks);
+        // undropped values and 1 / (1 - p) is applied to O at the end
         float pd[8];
 #pragma unroll
-        for (int x = 0; x < 8; ++x) pd[x] = (k8 >> x) & 1 ? sv[e + x] * dp.scale : 0.f;
+        for (int x = 0; x < 8; ++x) pd[x] = drop_kept(dp, keep[qh][2 * ks + (x >> 2)], x & 3) ? sv[e + x] : 0.f;
 #pragma unroll
         for (int x = 0; x < 4; ++x) pw[x] = pack_bf16x2(pd[2 * x], pd[2 * x + 1]);
       } else {
@@ -403,7 +402,9 @@ __device__ __forceinline__ void tile_step(char* smem, int j, const char* kp, con
   for (int qh = 0; qh < QH; ++qh) l[qh] = l[qh] * alpha[qh] + sum32(s[qh][0], s[qh][1]);
   if constexpr (DROP && AHEAD && NEXT) {
 #pragma unroll
-    for (int qh = 0; qh < QH; ++qh) keep[qh] = keep_next[qh];
+    for (int qh = 0; qh < QH; ++qh)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) keep[qh][c] = keep_next[qh][c];
   }
 
   wait_vm_barrier<T::VMCNT>();  // tile j+2 landed; tile j+3 may still be in flight
@@ -504,10 +505,10 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   f32x16 s0[QH][2], s1[QH][2];
   if constexpr (F8) scores_f8<D>(smem, krow0, h, qf, s0);
   else scores<D>(smem, krow0, h, qf, s0);
-  uint32_t keep[QH] = {};  // dropout keep bits of the current tile (tile 0's made here)
+  uint32_t keep[QH][8] = {};  // dropout random words of the current tile (tile 0's made here)
   if constexpr (DROP && !CAUSAL) {
 #pragma unroll
-    for (int qh = 0; qh < QH; ++qh) keep[qh] = drop_tile_keys(a.drop, (8 * h) >> 2, q0 + 32 * qh + l32, bh);
+    for (int qh = 0; qh < QH; ++qh) drop_row_words(a.drop, (8 * h) >> 2, q0 + 32 * qh + l32, bh, keep[qh]);
   }
 
   // Without the mask, an odd number of look-ahead steps takes its first one before the loop
@@ -556,7 +557,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
 #pragma unroll
   for (int qh = 0; qh < QH; ++qh) {
     const float lt = halves_sum(l[qh]);
-    const float inv = 1.f / lt;
+    const float inv = (DROP ? a.drop.scale : 1.f) / lt;  // dropout: kept P scaled by 1 / (1 - p)
     const int qi = q0 + 32 * qh + l32;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
