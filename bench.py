@@ -465,7 +465,13 @@ def extra_parts(fa, w, ff, bf, results, reps):
     for m in (False, True):
         t = time_launches(lambda: fa.fa_fwd_poly_exp2(q, k, v, o, lse, causal=m, scale=w.scale), reps)
         results[f"fwd_poly_exp2_{'causal' if m else 'nc'}_b16h16n2048d128"] = rate_entry(t, ff[m], "bf16")
-    del q, k, v, o, lse
+    # the persistent forward (per-XCD task queues) on the same inputs
+    log("[bench] fwd_persistent_b16h16n2048d128")
+    pws = torch.zeros(fa.fa_fwd_persistent_workspace_size(), dtype=torch.uint8, device="cuda")
+    for m in (False, True):
+        t = time_launches(lambda: fa.fa_fwd_persistent(q, k, v, o, lse, pws, causal=m, scale=w.scale), reps)
+        results[f"fwd_persistent_{'causal' if m else 'nc'}_b16h16n2048d128"] = rate_entry(t, ff[m], "bf16")
+    del q, k, v, o, lse, pws
     torch.cuda.empty_cache()
 
     # FP8 forward on the training shape: Q and K quantised to E4M3 beforehand (as the kernel

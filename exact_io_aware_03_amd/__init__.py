@@ -29,7 +29,7 @@ EXPORTED = (
     "fa_version", "fa_wave_efficiency", "fa_plan_splits", "fa_schedule_makespan", "fa_causal_tiles",
     "fa_fp8_scale_count", "fa_quantize_fp8", "fa_fwd_fp8", "fa_fwd_dropout", "fa_bwd_dropout",
     "fa_lpt_makespan", "fa_build_info", "fa_decode_noalloc", "fa_bwd_single_pass", "fa_fwd_poly_exp2",
-    "fa_exp2_poly",
+    "fa_exp2_poly", "fa_fwd_persistent", "fa_fwd_persistent_workspace_size",
 )
 
 _lib = None
@@ -58,6 +58,10 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd.restype = i
     L.fa_bwd_single_pass.argtypes = [vp] * 9 + [i] * 7 + [f, i, vp, sz, vp]
     L.fa_bwd_single_pass.restype = i
+    L.fa_fwd_persistent_workspace_size.argtypes = []
+    L.fa_fwd_persistent_workspace_size.restype = sz
+    L.fa_fwd_persistent.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp]
+    L.fa_fwd_persistent.restype = i
     L.fa_fwd_poly_exp2.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
     L.fa_fwd_poly_exp2.restype = i
     L.fa_exp2_poly.argtypes = [vp, vp, ctypes.c_long, vp]
@@ -140,6 +144,23 @@ def fa_fwd(q, k, v, o, lse, causal: bool = False, scale: float | None = None, st
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     _check(lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, int(causal),
                         scale, _dtype_code(q), _stream(stream)))
+
+
+def fa_fwd_persistent_workspace_size() -> int:
+    return int(lib().fa_fwd_persistent_workspace_size())
+
+
+def fa_fwd_persistent(q, k, v, o, lse, workspace, causal: bool = False, scale: float | None = None,
+                      stream=None) -> None:
+    """fa_fwd (bf16) from the persistent kernel with per-XCD task queues; `workspace` is a
+    zero-initialised device buffer of fa_fwd_persistent_workspace_size() bytes."""
+    _need_contig(q, k, v, o, lse, workspace)
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    _check(lib().fa_fwd_persistent(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
+                                   int(causal), scale, _dtype_code(q), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def fa_fwd_poly_exp2(q, k, v, o, lse, causal: bool = False, scale: float | None = None, stream=None) -> None:

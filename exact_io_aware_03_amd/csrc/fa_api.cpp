@@ -72,7 +72,7 @@ const char* fa_strerror(int code) {
 
 static int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
                       int Nq, int Nk, int d, int causal, float scale, int dtype, const fa::Dropout* drop,
-                      void* stream, bool poly = false) {
+                      void* stream, bool poly = false, int* ctr = nullptr) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_INVALID_ARG;
   int st = common_checks(B, Hq, Hkv, Nq, Nk, d, scale);
@@ -95,6 +95,10 @@ static int fwd_common(const void* q, const void* k, const void* v, void* o, floa
   if (tasks > INT_MAX) return FA_ERR_INVALID_ARG;
   a.n_tasks = (int)tasks;
   hipStream_t s = (hipStream_t)stream;
+  if (ctr) {
+    a.ctr = ctr;
+    return hip_status(fa::launch_fwd_persistent(a, d, s));
+  }
   if (poly) return hip_status(fa::launch_fwd_poly(a, d, s));
   if (drop && drop->t > 0) {
     a.drop = *drop;
@@ -106,6 +110,17 @@ static int fwd_common(const void* q, const void* k, const void* v, void* o, floa
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Nq,
            int Nk, int d, int causal, float scale, int dtype, void* stream) {
   return fwd_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, dtype, nullptr, stream);
+}
+
+size_t fa_fwd_persistent_workspace_size(void) { return align256(fa::kFwdPoolCounters * sizeof(int)); }
+
+int fa_fwd_persistent(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                      int Nq, int Nk, int d, int causal, float scale, int dtype, void* workspace, size_t ws_bytes,
+                      void* stream) {
+  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (!workspace || ws_bytes < fa_fwd_persistent_workspace_size() || !aligned16(workspace)) return FA_ERR_WORKSPACE;
+  return fwd_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, dtype, nullptr, stream, false,
+                    (int*)workspace);
 }
 
 int fa_fwd_poly_exp2(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,

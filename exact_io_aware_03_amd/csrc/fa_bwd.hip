@@ -479,12 +479,6 @@ __device__ __forceinline__ void dma_frag_p(char* dst, const uint16_t* src, long 
   }
 }
 
-__device__ __forceinline__ int xcc_id() {
-  int x;
-  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(x));
-  return x;
-}
-
 // LDS-only barrier: this wave's LDS accesses are done, then the workgroup barrier (vector memory
 // operations may stay in flight).
 __device__ __forceinline__ void lds_barrier() {

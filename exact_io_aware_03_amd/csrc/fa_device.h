@@ -126,6 +126,13 @@ __device__ __forceinline__ int xcd_contiguous_task(int wg, int n) {
   return x * per + (x < rem ? x : rem) + i;
 }
 
+// Index of the XCD (accelerator complex die) this wave runs on.
+__device__ __forceinline__ int xcc_id() {
+  int x;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(x));
+  return x;
+}
+
 // Causal task order over n_grp groups (heads) x n_lvl levels (level 0 = longest task). Every
 // XCD keeps a fixed set of groups and works through them in clusters of `cs` groups, longest
 // level first inside a cluster, with cs * n_lvl about the XCD's 32 compute units: the tasks

@@ -34,6 +34,10 @@ struct FwdArgs {
   const float* k_scale;
   int q_nblk, k_nblk;
   Dropout drop;  // dropout on P (bf16 path): threshold t > 0 selects the dropout instance
+  // persistent forward only: task queue heads [kFwdMaxPools] and the leaver count after them,
+  // zero between calls; n_pools queues (one per XCD, or one)
+  int* ctr;
+  int n_pools;
 };
 
 struct DecArgs {
@@ -103,6 +107,9 @@ hipError_t launch_fwd_f32(const FwdArgs& a, int d, hipStream_t s);
 hipError_t launch_fwd_fp8(const FwdArgs& a, int d, hipStream_t s);
 hipError_t launch_fwd_dropout(const FwdArgs& a, int d, hipStream_t s);
 hipError_t launch_fwd_poly(const FwdArgs& a, int d, hipStream_t s);
+constexpr int kFwdMaxPools = 8;          // persistent forward: task queues (one per XCD)
+constexpr int kFwdPoolCounters = 16;     // its counters: the queues, the leaver count, padding
+hipError_t launch_fwd_persistent(FwdArgs a, int d, hipStream_t s);
 hipError_t launch_exp2_poly(const float* x, float* y, long n, hipStream_t s);
 hipError_t launch_bwd_dropout(const BwdArgs& a, int d, hipStream_t s);
 constexpr int kFp8Block = 64;     // rows per FP8 quantisation block (one scale each)

@@ -63,6 +63,25 @@ enum fa_status {
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
            int Nq, int Nk, int d, int causal, float scale, int dtype, void* stream);
 
+/* Workspace bytes fa_fwd_persistent needs (256): its task-queue counters. They must be zero
+ * before a workspace's first use (allocate it zero-filled once); every call leaves them zero
+ * again, so any sequence of calls reuses one workspace without clearing. */
+size_t fa_fwd_persistent_workspace_size(void);
+
+/*
+ * Persistent forward (Lecture 21 notes §4.5): the result of fa_fwd (bf16), bit for bit, from
+ * one workgroup per compute unit that takes query-block tasks from a queue per XCD, in the
+ * order the one-shot grid gives that XCD (without the mask a contiguous run of a head's query
+ * blocks; with it longest first), and from the other XCDs' queues once its own is empty.
+ * dtype FA_BF16 only (others: FA_ERR_UNSUPPORTED); d in {64, 128}. workspace: at least
+ * fa_fwd_persistent_workspace_size() bytes, 16-byte aligned, zero before first use (else
+ * FA_ERR_WORKSPACE if null or short). Calls that share a workspace must not overlap (one
+ * stream, or synchronised).
+ */
+int fa_fwd_persistent(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                      int Nq, int Nk, int d, int causal, float scale, int dtype, void* workspace, size_t ws_bytes,
+                      void* stream);
+
 /* Workspace bytes fa_bwd needs: task-pool counters (256 bytes) and fp32 partial sums of dQ
  * (B * Hq * ceil(Nq / 64) blocks of 64 x d) at the start, then D = rowsum(dO * O) fp32
  * [B, Hq, Nq]. The first 256 + 256 * d * B * Hq * ceil(Nq / 64) bytes must be zero before a

@@ -59,6 +59,26 @@ def test_fwd_validation(kw, code):
     assert fwd(**kw) == code
 
 
+def fwd_persistent(ws=P, ws_bytes=256, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=64, causal=0, scale=0.125, dtype=1)
+    a.update(kw)
+    return fa.lib().fa_fwd_persistent(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"],
+                                      a["Nk"], a["d"], a["causal"], a["scale"], a["dtype"], ws, ws_bytes, None)
+
+
+def test_fwd_persistent_validation():
+    # 16 int counters (8 queues, the leaver count, padding), one 256-byte block
+    assert fa.fa_fwd_persistent_workspace_size() == 256
+    # bf16 only and the workspace, then the forward's own checks, all before any HIP call
+    assert fwd_persistent(q=None) == INVALID
+    assert fwd_persistent(d=96) == UNSUPPORTED
+    assert fwd_persistent(causal=1, Nk=9) == UNSUPPORTED
+    assert fwd_persistent(dtype=0) == UNSUPPORTED
+    assert fwd_persistent(ws=None) == WORKSPACE
+    assert fwd_persistent(ws_bytes=255) == WORKSPACE
+    assert fwd_persistent(ws=MIS) == WORKSPACE
+
+
 def bwd(ws=P, ws_bytes=None, **kw):
     a = dict(B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=64, causal=0, scale=0.125, dtype=1)
     a.update(kw)

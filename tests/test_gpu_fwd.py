@@ -38,9 +38,8 @@ SMALL = [
     (1, 129, 65, 8, 2, 64, False, "bf16"),
     (1, 1, 1, 1, 1, 128, False, "bf16"),       # a single key and query
     (1, 5, 1000, 2, 1, 64, False, "bf16"),
-    # more tasks than compute units, so workgroups of the persistent non-causal forward run
-    # several (batch, head, row block) tasks: ragged rows and keys with GQA, and the minimum of
-    # three key tiles at d = 64
+    # more (batch, head, row block) tasks than compute units: ragged rows and keys with GQA, and
+    # the minimum of three key tiles at d = 64
     (4, 700, 451, 32, 8, 128, False, "bf16"),
     (3, 300, 192, 64, 64, 64, False, "bf16"),
     (1, 256, 256, 1, 1, 64, False, "f32"),
