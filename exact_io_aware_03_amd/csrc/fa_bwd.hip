@@ -763,6 +763,10 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_fused_kernel(BwdArgs a) {
         s = mfma_32x32x16(ld16(qo + QB), ld16(kb), s);
         gg = mfma_32x32x16(ld16(qo + GB), ld16(kb + L::KT), gg);
       }
+      // the partial sum of this tile, stored by the previous adder at the end of its step
+      f32x16 dq;
+      if (rank != 0) load_tile(racc, lane, dq);
+      else zero16(dq);
       const int qw0 = q0 + 32 * qhalf;
       if (kw0 + 31 >= a.Nk || (a.causal && kw0 + 31 > qw0)) {
         const int first_row = key >= a.Nk ? 0x7fffffff : (a.causal ? key : 0);
@@ -784,10 +788,6 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_fused_kernel(BwdArgs a) {
           gg[r] = p * (gg[r] - dvv);  // dS
         }
       }
-      // the partial sum of this tile, stored by the previous adder at the end of its step
-      f32x16 dq;
-      if (rank != 0) load_tile(racc, lane, dq);
-      else zero16(dq);
       // ---- dV += P^T dO, dK += dS^T Q; dS^T (bf16) to LDS for the dQ product ----
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
