@@ -91,3 +91,34 @@ def test_persistent_full_sizes(name, causal):
     ro, rl = ora.forward(inp["q"], inp["k"], inp["v"], causal, w.scale, rows=rows)
     check("O[rows]", o[:, rows], ro[:, rows], "bf16", config=True)
     check("L[rows]", lse[:, :, rows], rl[:, :, rows], "bf16", is_lse=True)
+
+
+def test_persistent_two_streams_two_workspaces():
+    # two calls in flight at once on two streams, each with its own workspace: the queues of
+    # one call never hand out the other's tasks, and both results equal fa_fwd's
+    import torch
+
+    fa = _fa()
+    cases = [workloads.make_attention_inputs(4, 1000, 1000, 16, 4, 128, seed=3101),
+             workloads.make_attention_inputs(2, 1500, 1500, 8, 8, 64, seed=3102)]
+    dev = [tuple(to_dev(inp[n], "bf16") for n in ("q", "k", "v")) for inp in cases]
+    outs, refs = [], []
+    for (q, k, v), causal in zip(dev, (True, False)):
+        B, Nq, Hq, _ = q.shape
+        o1 = torch.empty_like(q)
+        l1 = torch.empty((B, Hq, Nq), dtype=torch.float32, device="cuda")
+        fa.fa_fwd(q, k, v, o1, l1, causal, None)
+        refs.append((o1, l1))
+        outs.append((torch.empty_like(q), torch.empty_like(l1)))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    wss = [torch.zeros(fa.fa_fwd_persistent_workspace_size(), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    for rep in range(3):
+        for i, ((q, k, v), causal) in enumerate(zip(dev, (True, False))):
+            with torch.cuda.stream(streams[i]):
+                fa.fa_fwd_persistent(q, k, v, outs[i][0], outs[i][1], wss[i], causal, None, stream=streams[i])
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert int(wss[i].count_nonzero()) == 0
+            assert torch.equal(outs[i][0], refs[i][0]) and torch.equal(outs[i][1], refs[i][1]), (rep, i)
+        say(f"  two streams, repeat {rep}: both identical to fa_fwd")
