@@ -51,3 +51,51 @@ def test_decode_noalloc_matches_decode_twice():
             ro, rl = ora.decode(inp["q"], inp["k"], inp["v"], inp["seqlens"], scale)
             check("O noalloc vs oracle", o2, ro, "bf16")
             check("L noalloc vs oracle", l2, rl, "bf16", is_lse=True)
+
+
+def test_decode_noalloc_under_graph_capture():
+    # the callers it is for: a HIP graph holds one call and replays it; every replay, with eager
+    # work between (another shape's call through the same scratch array, fills, syncs), gives
+    # the eager call's result bit for bit
+    import torch
+
+    import exact_io_aware_03_amd as fa
+
+    inp = workloads.make_decode_inputs(16, 16, 4, 2048, 128, seed=12, len_range=(1, 2048))
+    other = workloads.make_decode_inputs(5, 8, 8, 900, 64, seed=13, len_range=(1, 900))
+    scale = 1 / math.sqrt(128)
+    q, k, v = (to_dev(inp[n], "bf16") for n in ("q", "k", "v"))
+    lens = torch.from_numpy(inp["seqlens"]).cuda()
+    q2, k2, v2 = (to_dev(other[n], "bf16") for n in ("q", "k", "v"))
+    lens2 = torch.from_numpy(other["seqlens"]).cuda()
+    B, _, Hq, _ = q.shape
+    o_ref = torch.empty_like(q)
+    l_ref = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    fa.fa_decode_noalloc(q, k, v, lens, o_ref, l_ref, scale)  # eager; also finds the scratch address
+    o2 = torch.empty_like(q2)
+    l2 = torch.empty((q2.shape[0], q2.shape[2]), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    o, l = torch.empty_like(o_ref), torch.empty_like(l_ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fa.fa_decode_noalloc(q, k, v, lens, o, l, scale)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fa.fa_decode_noalloc(q, k, v, lens, o, l, scale)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        o.zero_()
+        l.zero_()
+        fa.fa_decode_noalloc(q2, k2, v2, lens2, o2, l2, 1 / math.sqrt(64))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        same = torch.equal(o, o_ref) and torch.equal(l, l_ref)
+        say(f"  graph replay {rep}: identical to the eager call: {same}")
+        assert same
+    ro, rl = ora.decode(inp["q"], inp["k"], inp["v"], inp["seqlens"], scale)
+    check("O graph replay vs oracle", to_np(o), ro, "bf16")
+    check("L graph replay vs oracle", to_np(l), rl, "bf16", is_lse=True)
