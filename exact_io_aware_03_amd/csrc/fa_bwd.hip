@@ -419,9 +419,14 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(BwdArgs a) {
 //    writes dQ in bf16 and stores zeros, so the area is all zero between calls. A value is read
 //    only once its writer has stored it, and a writer never waits for a reader, so a wait chain
 //    always ends at a block's first adder.
-//  * Visiting order. Causal: key block j sees query blocks i >= 2j, walks them upwards and adds
-//    in order of decreasing j (shortest task first): j reaches block i 2 + 2g steps after j + 1
-//    did, so the first writer of every block never waits. Without the mask: the blocks over the
+//  * Visiting order. Causal: key block j sees query blocks i >= 2j and walks them downwards from
+//    the last, the G heads of the group at each block, adding in order of decreasing j (tasks
+//    are taken shortest first). Every key block reaches a block the same number of steps after
+//    its own start, so j arrives after j + 1, which was taken before it, and a block's adders
+//    follow one another at the pace tasks are taken: its partial sum and Q/dO tiles are live
+//    for a few steps rather than from the first adder's visit to key block 0's, and fewer
+//    blocks are live at once than the L2 holds. The first writer of a block never waits.
+//    Without the mask: the blocks over the
 //    G heads of the group (M of them) are taken in windows of Tc (the number of key blocks); in
 //    a window key block j starts j blocks in and wraps, so each block gets one adder per step
 //    and is finished within Tc steps (the window's partial sums and Q/dO tiles stay in L2). The
@@ -702,10 +707,13 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_fused_kernel(BwdArgs a) {
     };
     auto advance = [&](int& sa, int& sb) {
       if (a.causal) {
-        if (++sb == n_tr) {
-          sb = qb_first;
-          ++sa;
+        if (++sa == a.G) {
+          sa = 0;
+          --sb;
         }
+        // uniform, so that the tile addresses built from them stay in scalar registers
+        sa = __builtin_amdgcn_readfirstlane(sa);
+        sb = __builtin_amdgcn_readfirstlane(sb);
       } else if (++sb == min(n_tc, m_all - sa * n_tc)) {
         sb = 0;
         ++sa;
@@ -714,7 +722,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_fused_kernel(BwdArgs a) {
     auto vis_g = [](int v) { return (v >> 9) & 127; };
     auto vis_i = [](int v) { return (int)((unsigned)v >> 16); };
     auto vis_rank = [](int v) { return v & 255; };
-    int sa = 0, sb = a.causal ? qb_first : 0;
+    int sa = 0, sb = a.causal ? n_tr - 1 : 0;
     int cur = make_vis(sa, sb);
     auto tile_index = [&](int v) {  // (query head, block, wave) tile of dQ
       return ((bhq0 + vis_g(v)) * n_tr + vis_i(v)) * kWaves + wave;

@@ -39,14 +39,18 @@ def task_steps(causal, G, n_tr, n_tc, j):
         f = w0 + o
         return (f // n_tr, f % n_tr, rank, rank == n_tc - 1)
 
-    sa, sb = 0, (qb_first if causal else 0)
+    # causal: query blocks from the last one down, the G heads at each block
+    sa, sb = 0, (n_tr - 1 if causal else 0)
     out = []
     for _ in range(n_steps):
         out.append(make(sa, sb))
+        if causal:
+            sa += 1
+            if sa == G:
+                sa, sb = 0, sb - 1
+            continue
         sb += 1
-        if causal and sb == n_tr:
-            sb, sa = qb_first, sa + 1
-        elif not causal and sb == min(n_tc, m_all - sa * n_tc):
+        if sb == min(n_tc, m_all - sa * n_tc):
             sb, sa = 0, sa + 1
     return out
 
@@ -111,3 +115,15 @@ def test_schedule(B, Hkv, G, Nq, Nk, causal):
 @pytest.mark.parametrize("B,Hkv,G,Nq,Nk", [(2, 2, 1, 300, 300), (1, 1, 4, 1000, 1000)])
 def test_causal_needs_no_coresidency(B, Hkv, G, Nq, Nk):
     run(B, Hkv, G, Nq, Nk, True, per_xcd=1, seed=3)
+
+
+@pytest.mark.parametrize("G,N", [(1, 2048), (4, 1000), (3, 333)])
+def test_causal_blocks_reached_at_the_same_offset(G, N):
+    # every key block reaches query block (g, i) the same number of steps after its start, so the
+    # adders of a block arrive in the order their tasks were taken (largest j first) and follow
+    # one another closely
+    n_tr, n_tc = -(-N // BQ), -(-N // BK)
+    for j in range(n_tc):
+        for s, (g, i, rank, _) in enumerate(task_steps(True, G, n_tr, n_tc, j)):
+            assert s == (n_tr - 1 - i) * G + g
+            assert rank == min(n_tc, i // 2 + 1) - 1 - j
