@@ -302,7 +302,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(BwdArgs a) {
         const float p = fast_exp2(fmaf(s[i], a.c, -lv * kLog2e));
         if constexpr (DROP) {
           const bool z = drop_kept(a.drop, kw[x & 3], 2 * hi + (x >> 2));
-          s[i] = z ? p : 0.f;                                   // P Z; dV takes 1 / (1 - p) at the end
+          s[i] = keep_or_zero(z, p);  // P Z; dV takes 1 / (1 - p) at the end
           g[i] = p * fmaf(z ? g[i] : 0.f, a.drop.scale, -dvv);  // dS = P (dP Z / (1 - p) - D)
         } else {
           s[i] = p;                  // P

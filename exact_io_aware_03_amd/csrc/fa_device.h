@@ -198,6 +198,15 @@ __device__ __forceinline__ bool drop_kept(const Dropout& dp, uint32_t w, int i) 
   return ((w >> (8 * i)) & 255u) >= dp.t;
 }
 
+// x where the element is kept, else 0, selected in fp32: the empty asm keeps the compiler from
+// moving the select past the bf16 conversion that follows (one conversion per element and a
+// perm per pair instead of one conversion per pair)
+__device__ __forceinline__ float keep_or_zero(bool kept, float x) {
+  float r = kept ? x : 0.f;
+  asm("" : "+v"(r));
+  return r;
+}
+
 // 4 x 4 transpose of words across a quad (lane r = row & 3): on entry lane r holds a[k],
 // k = 0..3; on exit b[c] is lane c's a[r]. Two exchanges: with lane r ^ 1 each lane keeps
 // the words of rows of its own parity and trades the others, then with lane r ^ 2 it keeps

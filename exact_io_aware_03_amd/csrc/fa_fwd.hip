@@ -380,7 +380,7 @@ __device__ __forceinline__ void tile_step(char* smem, int j, const char* kp, con
         // undropped values and 1 / (1 - p) is applied to O at the end
         float pd[8];
 #pragma unroll
-        for (int x = 0; x < 8; ++x) pd[x] = drop_kept(dp, keep[qh][2 * ks + (x >> 2)], x & 3) ? sv[e + x] : 0.f;
+        for (int x = 0; x < 8; ++x) pd[x] = keep_or_zero(drop_kept(dp, keep[qh][2 * ks + (x >> 2)], x & 3), sv[e + x]);
 #pragma unroll
         for (int x = 0; x < 4; ++x) pw[x] = pack_bf16x2(pd[2 * x], pd[2 * x + 1]);
       } else {
