@@ -426,18 +426,17 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(BwdArgs a) {
 //    follow one another at the pace tasks are taken: its partial sum and Q/dO tiles are live
 //    for a few steps rather than from the first adder's visit to key block 0's, and fewer
 //    blocks are live at once than the L2 holds. The first writer of a block never waits.
-//    Without the mask: the blocks over the
-//    G heads of the group (M of them) are taken in windows of Tc (the number of key blocks); in
-//    a window key block j starts j blocks in and wraps, so each block gets one adder per step
-//    and is finished within Tc steps (the window's partial sums and Q/dO tiles stay in L2). The
-//    order is circular, so the Tc workgroups of a head must run together (Tc <= 16, half an
-//    XCD); ties in a short last window are ordered by decreasing j.
-//  * Pools are taken in order and a task only waits for tasks of its own head taken before it
-//    (causal) or alongside it, so the waits always end; each wait is also bounded: a wave whose
-//    wait outlasts 0.2 s (possible only if the area was not zero at the start or the hardware did
-//    not run a head's workgroups together) stops waiting for the rest of the launch, the result
-//    is then wrong, and the event is counted in a word of the workspace that the kernel never
-//    clears, so a caller checking that the counters are zero after a call sees it.
+//    Without the mask: every key block walks all M = G Tr blocks of the group in the same
+//    order, and tasks are taken in decreasing j too, so key block j follows j + 1 through the
+//    blocks a fraction of a step behind it (a convoy that forms once, at the start). An order
+//    with one adder per block per step needs a circular order of the adders, and so all Tc
+//    workgroups of a head running together, which two calls on two streams can prevent.
+//  * Pools are taken in order and a task only waits for a task of its own head taken before
+//    it, so the waits end with any number of workgroups resident; each wait is also bounded: a
+//    wave whose wait outlasts 0.2 s (possible only if the area was not zero at the start) stops
+//    waiting for the rest of the launch, the result is then wrong, and the event is counted in a
+//    word of the workspace that the kernel never clears, so a caller checking that the counters
+//    are zero after a call sees it.
 //  * Per step, after the dK/dV products: each wave writes its dS^T (32 keys x 32 rows, bf16) to
 //    LDS; after a barrier each wave computes dQ^T for its 32 rows x 32 dims of the 64 x 128 block
 //    over all 128 keys, K^T and dS^T both read transposed with ds_read_b64_tr_b16. K and V keep
@@ -448,7 +447,6 @@ constexpr int kMaxPools = 8;          // task pools: one per XCD (a.ctr[0..7]; a
 constexpr int kTimeoutCounter = kBwdPoolCounters - 1;  // waits that ran out (left nonzero)
 static_assert(kMaxPools + 1 < kTimeoutCounter, "pool counters");
 constexpr int kCusPerXcd = 32;
-constexpr int kFusedMaxTeam = 16;     // key blocks of a head that must run together (no mask)
 constexpr int kMaxAdders = 255;       // 8-bit adder tags
 constexpr long kWaitTicks = 20000000;  // bounded waits: 0.2 s of the 100 MHz real-time counter
 
@@ -646,7 +644,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_fused_kernel(BwdArgs a) {
     if (task >= pool_tasks) break;
     const int bhk = pool + a.n_pools * (task / n_tc);
     const int jj = task % n_tc;
-    const int j = a.causal ? n_tc - 1 - jj : jj;  // causal: shortest task of the head first
+    const int j = n_tc - 1 - jj;  // decreasing j: with the mask the shortest task first
     const int b = bhk / a.Hkv, hk = bhk % a.Hkv;
     const int kv0 = j * BK;
     const int kw0 = kv0 + slice * 32;
@@ -665,13 +663,12 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_fused_kernel(BwdArgs a) {
     const int qb_first = a.causal ? kv0 / BQ : 0;
     const int per_head = n_tr - qb_first;
     const int n_steps = a.G * per_head;
-    const int m_all = a.G * n_tr;        // without the mask: blocks over the G heads
     const int bhq0 = b * a.Hq + hk * a.G;
 
     // A step's visit packed in one word: bits 0-7 this key block's rank among the adders of the
     // block (0 = first), bit 8 whether it is the last, bits 9-15 the query head g within the
     // group, bits 16-31 the 64-row block i. The walk state (sa, sb) is (g, i) with the mask and
-    // (window, step within it) without.
+    // (unused, g Tr + i) without.
     auto make_vis = [&](int sa, int sb) {
       int g, i, rank;
       bool last;
@@ -682,26 +679,10 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_fused_kernel(BwdArgs a) {
         rank = cnt - 1 - j;
         last = j == 0;
       } else {
-        const int w0 = sa * n_tc, len = min(n_tc, m_all - w0);  // window [w0, w0 + len)
-        int o;
-        if (len == n_tc) {
-          o = j + sb;
-          if (o >= n_tc) o -= n_tc;
-          rank = sb;  // one adder per step
-        } else {
-          // short last window: key blocks j = j' (mod len) arrive together, larger j first
-          o = (j + sb) % len;
-          rank = (n_tc - 1 - j) / len;
-          for (int c = 0; c < sb; ++c) {
-            int r = o - c;
-            if (r < 0) r += len;
-            rank += (n_tc - 1 - r) / len + 1;
-          }
-        }
-        last = rank == n_tc - 1;
-        const int f = w0 + o;
-        g = f / n_tr;
-        i = f - g * n_tr;
+        g = sb / n_tr;
+        i = sb - g * n_tr;
+        rank = n_tc - 1 - j;
+        last = j == 0;
       }
       return rank | (last ? 256 : 0) | (g << 9) | (i << 16);
     };
@@ -714,9 +695,8 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_fused_kernel(BwdArgs a) {
         // uniform, so that the tile addresses built from them stay in scalar registers
         sa = __builtin_amdgcn_readfirstlane(sa);
         sb = __builtin_amdgcn_readfirstlane(sb);
-      } else if (++sb == min(n_tc, m_all - sa * n_tc)) {
-        sb = 0;
-        ++sa;
+      } else {
+        ++sb;
       }
     };
     auto vis_g = [](int v) { return (v >> 9) & 127; };
@@ -1206,10 +1186,9 @@ hipError_t launch_single_pass(BwdArgs a, hipStream_t s) {
 
 }  // namespace
 
-// Without the mask a head's key blocks must run together (at most half an XCD); with it, the
-// adder tags limit a block to 255 key blocks.
+// The 8-bit adder tags limit a block to 255 key blocks.
 bool bwd_single_pass_supported(const BwdArgs& a, int d) {
-  return d == 128 && (a.causal ? a.n_kvblk <= kMaxAdders : a.n_kvblk <= kFusedMaxTeam);
+  return d == 128 && a.n_kvblk <= kMaxAdders;
 }
 
 hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t s) {

@@ -106,13 +106,14 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
 /*
  * The same backward in one key-block-outer pass that forms all five products (dQ is not
  * recomputed): each 64-row block's dQ is summed in fp32 in the workspace by the key blocks in a
- * fixed order, shortest task first with the causal mask, each partial sum tagged with its adder
- * count ("Flash Attention 3/4 笔记" (KaiSpace), deterministic backward; dQ accumulated over key
- * blocks as in Lecture 21 notes §2.6, exercise 6). Results are reproducible run to run and agree
- * with fa_bwd up to rounding. Arguments, workspace and its contract as for fa_bwd. Supported:
- * dtype FA_BF16, d = 128, and Nk <= 2048 without the causal mask (a head's 16 key-block
- * workgroups must run at the same time) or Nk <= 32640 with it; other shapes return
- * FA_ERR_UNSUPPORTED before any device work.
+ * fixed order (decreasing key block, tasks taken in that order; shortest task first with the
+ * causal mask), each partial sum tagged with its adder count ("Flash Attention 3/4 笔记"
+ * (KaiSpace), deterministic backward; dQ accumulated over key blocks as in Lecture 21 notes
+ * §2.6, exercise 6). A task only waits for tasks taken before it, so the call completes with any
+ * number of its workgroups resident (other work on other streams included). Results are
+ * reproducible run to run and agree with fa_bwd up to rounding. Arguments, workspace and its
+ * contract as for fa_bwd. Supported: dtype FA_BF16, d = 128 and Nk <= 32640 (255 key blocks:
+ * 8-bit adder tags); other shapes return FA_ERR_UNSUPPORTED before any device work.
  */
 int fa_bwd_single_pass(const void* q, const void* k, const void* v, const void* o, const void* dout,
                        const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d,

@@ -102,7 +102,7 @@ def test_bwd_single_pass_validation():
     # shapes the single pass does not take are refused before any device work
     assert bwd_single(d=64) == UNSUPPORTED
     assert bwd_single(dtype=0) == UNSUPPORTED
-    assert bwd_single(Nk=2049) == UNSUPPORTED               # 17 key blocks without the mask
+    assert bwd_single(Nk=32641) == UNSUPPORTED              # 256 key blocks without the mask
     assert bwd_single(Nq=32641, Nk=32641, causal=1, Hq=1) == UNSUPPORTED  # 256 key blocks with it
     assert bwd_single(ws=None) == WORKSPACE
     assert bwd_single(ws_bytes=fa.fa_bwd_workspace_size(1, 2, 8, 128) - 1) == WORKSPACE

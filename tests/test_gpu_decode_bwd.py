@@ -134,10 +134,10 @@ def run_fwd_bwd(inp, causal, scale, ws=None, single_pass=False):
 
 
 def single_pass_supported(Nk, d, causal):
-    """Shapes fa_bwd_single_pass takes: d = 128 and at most 16 key blocks of 128 without the mask
-    (the workgroups of a head run together) or 255 with it (8-bit adder tags)."""
+    """Shapes fa_bwd_single_pass takes: d = 128 and at most 255 key blocks of 128 (8-bit adder
+    tags), with or without the mask."""
     n_tc = -(-Nk // 128)
-    return d == 128 and n_tc <= (255 if causal else 16)
+    return d == 128 and n_tc <= 255
 
 
 @pytest.mark.parametrize(
@@ -156,7 +156,8 @@ def single_pass_supported(Nk, d, causal):
         (1, 520, 70, 2, 1, 64, False, None),    # more query rows than keys
         (1, 1, 1, 1, 1, 128, False, None),      # one query, one key: dS = 0, dV = dO
         (1, 256, 2048, 4, 2, 128, False, None),  # 16 key blocks, fewer query blocks than key blocks
-        (1, 64, 2100, 2, 1, 128, False, None),  # 17 key blocks without the mask: the two-kernel path
+        (1, 64, 2100, 2, 1, 128, False, None),  # 17 key blocks without the mask, more than half an XCD
+        (1, 64, 32769, 1, 1, 128, False, None),  # 257 key blocks: past the single pass's 8-bit tags
         (1, 1100, 1100, 2, 1, 128, True, None),  # causal GQA, 9 key blocks, ragged
     ],
 )
@@ -251,3 +252,40 @@ def test_bwd_and_fwd_are_reproducible(single_pass):
         runs.append([t.clone() for t in (o, lse, dq, dk, dv)])
     for a, b in zip(*runs):
         assert torch.equal(a, b)
+
+
+def test_single_pass_two_streams_two_workspaces():
+    # two single-pass calls in flight at once on two streams (one per mask, 16 key blocks per
+    # head), each with its own workspace: a task only waits for tasks of its own call taken before
+    # it, so neither call needs all of its workgroups resident, and both results are bit-identical
+    # to the same call run alone
+    import torch
+
+    fa = _fa()
+    cases = [(workloads.make_attention_inputs(2, 2048, 2048, 8, 4, 128, seed=5101, with_do=True), False),
+             (workloads.make_attention_inputs(2, 2048, 2048, 8, 8, 128, seed=5102, with_do=True), True)]
+    dev, refs, outs, wss = [], [], [], []
+    for inp, causal in cases:
+        q, k, v, do = (to_dev(inp[n], "bf16") for n in ("q", "k", "v", "do"))
+        o, lse = fa.forward(q, k, v, causal=causal, scale=0.09)
+        B, Nq, Hq, d = q.shape
+        ws = torch.zeros(fa.fa_bwd_workspace_size(B, Hq, Nq, d), dtype=torch.uint8, device="cuda")
+        r = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+        fa.fa_bwd_single_pass(q, k, v, o, do, lse, *r, ws, causal, 0.09)
+        dev.append((q, k, v, o, do, lse, causal))
+        refs.append(r)
+        outs.append([torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)])
+        wss.append((ws, bwd_zeroed_bytes(B, Hq, Nq, d)))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(3):
+        for i, (q, k, v, o, do, lse, causal) in enumerate(dev):
+            with torch.cuda.stream(streams[i]):
+                fa.fa_bwd_single_pass(q, k, v, o, do, lse, *outs[i], wss[i][0], causal, 0.09, stream=streams[i])
+        torch.cuda.synchronize()
+        for i in range(2):
+            ws, nc = wss[i]
+            assert int(torch.count_nonzero(ws[:nc])) == 0, (rep, i)
+            for a, b in zip(outs[i], refs[i]):
+                assert torch.equal(a, b), (rep, i)
+        say(f"  two streams, repeat {rep}: both identical to the calls run alone")

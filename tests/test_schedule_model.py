@@ -5,8 +5,8 @@ visiting order of query blocks; each key block's rank among a block's adders; ta
 reader waits for and a writer sets once its step is done) and run under random interleavings
 of the workgroups of each XCD: every block's ranks are 0 .. count-1 once each, the last adder is
 marked, all tags return to zero, and the run never reaches a state where no workgroup can move
-(no deadlock) -- with 32 workgroups per XCD, and with the causal mask even with one. The
-adders of a block are key blocks 0 .. Tc-1 without the mask and 0 .. floor(i/2) with it
+(no deadlock) -- with 32 workgroups per XCD and with as few as one, with and without the mask.
+The adders of a block are key blocks 0 .. Tc-1 without the mask and 0 .. floor(i/2) with it
 (Lecture 21 notes §2.6: key block j sees query rows from 128 j on; 64-row query blocks).
 """
 
@@ -19,7 +19,6 @@ BQ, BK = 64, 128
 
 def task_steps(causal, G, n_tr, n_tc, j):
     """(g, i, rank, last) for each step of key block j's task, as the kernel walks them."""
-    m_all = G * n_tr
     qb_first = (j * BK) // BQ if causal else 0
     n_steps = G * (n_tr - qb_first)
 
@@ -28,16 +27,8 @@ def task_steps(causal, G, n_tr, n_tc, j):
             g, i = sa, sb
             cnt = min(n_tc, (BQ * i + BQ - 1) // BK + 1)
             return (g, i, cnt - 1 - j, j == 0)
-        w0 = sa * n_tc
-        ln = min(n_tc, m_all - w0)
-        if ln == n_tc:
-            o = (j + sb) % n_tc
-            rank = sb
-        else:  # a short last window: key blocks equal mod ln arrive together, larger j first
-            o = (j + sb) % ln
-            rank = (n_tc - 1 - j) // ln + sum((n_tc - 1 - (o - c) % ln) // ln + 1 for c in range(sb))
-        f = w0 + o
-        return (f // n_tr, f % n_tr, rank, rank == n_tc - 1)
+        # without the mask every key block walks the G * Tr blocks in the same order
+        return (sb // n_tr, sb % n_tr, n_tc - 1 - j, j == 0)
 
     # causal: query blocks from the last one down, the G heads at each block
     sa, sb = 0, (n_tr - 1 if causal else 0)
@@ -50,8 +41,6 @@ def task_steps(causal, G, n_tr, n_tc, j):
                 sa, sb = 0, sb - 1
             continue
         sb += 1
-        if sb == min(n_tc, m_all - sa * n_tc):
-            sb, sa = 0, sa + 1
     return out
 
 
@@ -68,7 +57,7 @@ def run(B, Hkv, G, Nq, Nk, causal, per_xcd=32, n_pools=8, seed=0):
         assert [r for r, last in lst if last] == [len(lst) - 1]
         assert len(lst) == (min(n_tc, i // 2 + 1) if causal else n_tc)
     rng = random.Random(seed)
-    pools = [[(h, n_tc - 1 - jj if causal else jj) for h in range(p, heads, n_pools) for jj in range(n_tc)]
+    pools = [[(h, n_tc - 1 - jj) for h in range(p, heads, n_pools) for jj in range(n_tc)]
              for p in range(n_pools)]
     grab, tag = [0] * n_pools, {}
     wgs = [{"pool": p, "task": None} for p in range(n_pools) for _ in range(per_xcd)]
@@ -127,3 +116,9 @@ def test_causal_blocks_reached_at_the_same_offset(G, N):
         for s, (g, i, rank, _) in enumerate(task_steps(True, G, n_tr, n_tc, j)):
             assert s == (n_tr - 1 - i) * G + g
             assert rank == min(n_tc, i // 2 + 1) - 1 - j
+
+
+@pytest.mark.parametrize("B,Hkv,G,Nq,Nk", [(1, 1, 1, 2048, 2048), (2, 2, 2, 300, 4000), (1, 1, 1, 64, 2100), (3, 2, 3, 333, 2000)])
+@pytest.mark.parametrize("per_xcd", [1, 5, 32])
+def test_noncausal_any_residency(B, Hkv, G, Nq, Nk, per_xcd):
+    run(B, Hkv, G, Nq, Nk, False, per_xcd=per_xcd, seed=per_xcd + Nk)
