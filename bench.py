@@ -14,7 +14,9 @@ per part, 10 untimed launches then 50 timed ones, reported as median, minimum an
 roofline uses the mean launch duration). The fp64 CPU oracle is timed on a bounded sample of the
 training-shape forward (`cpu_baseline`), and on a bounded sample of each of the five workloads
 beside the GPU figures (`cpu_baseline.per_workload`). Inputs are the seeded synthetic tensors of
-workloads.py, resident in device memory before any timed region. One JSON line on stdout.
+workloads.py, resident in device memory before any timed region. After the timed parts the
+step runs back to back for about 3 s while `amd-smi metric` samples the XCD clocks and the
+socket power (`gpu_state`; null where the tool is missing or fails). One JSON line on stdout.
 """
 
 from __future__ import annotations
@@ -23,7 +25,10 @@ import argparse
 import json
 import math
 import os
+import shutil
+import subprocess
 import sys
+import threading
 import time
 
 import numpy as np
@@ -106,6 +111,65 @@ def rate_entry(ms_list, work, kind):
         if kind != "bf16":
             st["peak"] = round(peak, 1)
     return st
+
+
+def _smi_sample():
+    """One `amd-smi metric` reading of GPU 0: the gfx clock of each XCD (MHz) and the socket
+    power (W); None if the tool is missing or its output is not what is expected."""
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return None
+    try:
+        r = subprocess.run([exe, "metric", "-g", "0", "-c", "-p", "--json"], capture_output=True, text=True,
+                           timeout=30)
+    except (OSError, subprocess.TimeoutExpired):
+        return None
+    i = r.stdout.find("{")
+    if r.returncode != 0 or i < 0:
+        return None
+    try:
+        g = json.loads(r.stdout[i:])["gpu_data"][0]
+        clk = [float(v["clk"]["value"]) for name, v in g["clock"].items()
+               if name.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
+        pw = g["power"]["socket_power"]
+        power = float(pw["value"]) if isinstance(pw, dict) else None
+    except (ValueError, KeyError, IndexError, TypeError):
+        return None
+    return {"gfx_mhz": clk, "power_w": power} if clk else None
+
+
+def gpu_state(step, seconds=3.0):
+    """Clock and power while the step runs back to back: a thread takes amd-smi readings (child
+    processes) until the load ends; only readings that finished under load count."""
+    import torch
+
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        time.sleep(0.5)  # the clocks settle under the load first
+        while not stop.is_set():
+            s = _smi_sample()
+            if s is None:
+                return
+            if not stop.is_set():
+                samples.append(s)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=40)
+    if not samples:
+        return None
+    clk = [c for s in samples for c in s["gfx_mhz"]]
+    pw = [s["power_w"] for s in samples if s["power_w"] is not None]
+    return {"source": "amd-smi metric -c -p", "load": "the bench step back to back for %.0f s" % seconds,
+            "samples": len(samples), "gfx_mhz_median": float(np.median(clk)), "gfx_mhz_min": min(clk),
+            "gfx_mhz_max": max(clk), "socket_power_w_median": float(np.median(pw)) if pw else None}
 
 
 def csrc_sha256():
@@ -243,6 +307,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="only the training-shape forward step")
     ap.add_argument("--reps", type=int, default=50, help="timed launches per part (after 10 untimed)")
+    ap.add_argument("--no-smi", action="store_true", help="skip the amd-smi clock and power sampling")
     ap.add_argument("--calib", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -320,6 +385,7 @@ def main():
     dom_call = "%s %s" % ("fa_fwd" if dom[0] == "fwd" else "fa_bwd", "causal" if dom[1] else "non-causal")
     dom_name = {"fwd": "fwd_bf16_kernel<128,%s>" % ("true" if dom[1] else "false"),
                 "bwd": "fa_bwd %s (%s)" % ("causal" if dom[1] else "non-causal", BWD_KERNELS)}[dom[0]]
+    state = None if args.no_smi else gpu_state(step)
     del q, k, v, do, o, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
 
@@ -345,6 +411,7 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(dom_call)},
         "results": results,
+        "gpu_state": state,
         "build": fa.build_info(),
     }
     if not args.no_cpu:
