@@ -1,6 +1,7 @@
 """GPU parity of decode (fa_decode) and backward (fa_bwd) through the C ABI vs the fp64 oracle."""
 
 import math
+import time
 
 import numpy as np
 import pytest
@@ -289,3 +290,43 @@ def test_single_pass_two_streams_two_workspaces():
             for a, b in zip(outs[i], refs[i]):
                 assert torch.equal(a, b), (rep, i)
         say(f"  two streams, repeat {rep}: both identical to the calls run alone")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_single_pass_bounded_wait_reports_a_broken_workspace(causal):
+    # A workspace whose task-pool counters do not start at zero breaks the call's contract: every
+    # pool skips its first task, so some blocks never get their first adder and the adders after
+    # it wait for a tag that never comes. Each such wait ends after 0.2 s, the wave stops waiting
+    # for the rest of the launch, the kernel still finishes, the event is counted in the word the
+    # kernel never clears, and the last workgroup still resets the pool counters. A call on a
+    # zeroed workspace afterwards is exact again (bit-identical to a clean run).
+    import torch
+
+    fa = _fa()
+    inp = workloads.make_attention_inputs(1, 512, 512, 16, 16, 128, seed=5201, with_do=True)
+    q, k, v, do = (to_dev(inp[n], "bf16") for n in ("q", "k", "v", "do"))
+    o, lse = fa.forward(q, k, v, causal=causal, scale=0.09)
+    B, Nq, Hq, d = q.shape
+    nc = bwd_zeroed_bytes(B, Hq, Nq, d)
+    ws = torch.zeros(fa.fa_bwd_workspace_size(B, Hq, Nq, d), dtype=torch.uint8, device="cuda")
+    ref = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+    fa.fa_bwd_single_pass(q, k, v, o, do, lse, *ref, ws, causal, 0.09)
+    torch.cuda.synchronize()
+    ctr = ws[:64].view(torch.int32)
+    assert int(torch.count_nonzero(ws[:nc])) == 0
+    ctr[:8] = 1  # the eight task-pool counters
+    out = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+    t0 = time.perf_counter()
+    fa.fa_bwd_single_pass(q, k, v, o, do, lse, *out, ws, causal, 0.09)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    c = ctr.tolist()
+    say(f"  broken workspace: call returned after {dt:.2f} s, waits that ran out: {c[15]}, counters {c[:9]}")
+    assert c[15] > 0
+    assert c[:9] == [0] * 9
+    ws.zero_()
+    fa.fa_bwd_single_pass(q, k, v, o, do, lse, *out, ws, causal, 0.09)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(ws[:nc])) == 0
+    for a, b in zip(out, ref):
+        assert torch.equal(a, b)
