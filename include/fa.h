@@ -88,7 +88,8 @@ int fa_fwd_persistent(const void* q, const void* k, const void* v, void* o, floa
  * workspace's first use (allocate it zero-filled once); every call leaves them zero again, so
  * calls with the same B, Hq, Nq and d reuse a workspace without clearing (the layout moves
  * with them: zero it again before a call with other values), and calls that share one must not
- * overlap. D needs no initial contents. */
+ * overlap. After a call that returned FA_ERR_HIP, zero it again too. D needs no initial
+ * contents. */
 size_t fa_bwd_workspace_size(int B, int Hq, int Nq, int d);
 
 /*
@@ -113,7 +114,11 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
  * number of its workgroups resident (other work on other streams included). Results are
  * reproducible run to run and agree with fa_bwd up to rounding. Arguments, workspace and its
  * contract as for fa_bwd. Supported: dtype FA_BF16, d = 128 and Nk <= 32640 (255 key blocks:
- * 8-bit adder tags); other shapes return FA_ERR_UNSUPPORTED before any device work.
+ * 8-bit adder tags); other shapes return FA_ERR_UNSUPPORTED before any device work. Every wait
+ * for a partial sum is bounded: a wait that outlasts 0.2 s (possible only if the zeroed region
+ * was not zero at the call) ends, the results of that call are then wrong, and the event is
+ * counted in int32 word 15 of the workspace, which the kernel never clears (a caller that reads
+ * it after the stream has passed the call sees the failure; zero the workspace before reuse).
  */
 int fa_bwd_single_pass(const void* q, const void* k, const void* v, const void* o, const void* dout,
                        const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d,
