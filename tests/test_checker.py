@@ -47,3 +47,25 @@ def test_check_plain_bound_for_the_stated_workloads():
     got[7] = ref[7] + 0.04
     with pytest.raises(AssertionError):
         check("edge", got, ref, "bf16")  # more than one spacing (0.031) fails
+
+
+def test_terms_widen_the_bound_only_by_their_first_order_size():
+    # an output that is a cancelling sum: |ref| = 2 but its rounded terms add up to T = 40, so
+    # the method's bf16 rounding may move it by up to 2^-8 (40 + 2) = 0.164
+    rng = np.random.Generator(np.random.PCG64(5))
+    ref = rng.standard_normal(4096) * 0.5
+    terms = np.abs(ref) + 0.1
+    ref[11], terms[11] = 2.0, 40.0
+    got = ref.copy()
+    got[11] += 0.15
+    check("cancelling", got, ref, "bf16", terms=terms)  # inside u (T + |ref|)
+    with pytest.raises(AssertionError):
+        check("cancelling", got, ref, "bf16")  # without the terms: 2e-2 at |ref| = 2
+    with pytest.raises(AssertionError):
+        check("cancelling", got, ref, "bf16", config=True, terms=terms)  # the stated workloads ignore them
+    got[11] = ref[11] + 0.2
+    with pytest.raises(AssertionError):
+        check("cancelling", got, ref, "bf16", terms=terms)  # past u (T + |ref|)
+    got = ref + 0.05 * rng.choice([-1.0, 1.0], size=ref.size)  # a widespread error past 2e-2
+    with pytest.raises(AssertionError):
+        check("wrong", got, ref, "bf16", terms=terms)
