@@ -5,4 +5,4 @@ leg of bench.py, never by the product library, which must fail loudly if its HIP
 missing rather than fall back to anything here.
 """
 
-from . import attention, brute, dropout, fp8  # noqa: F401
+from . import attention, brute, dropout, fp8, rounding  # noqa: F401
