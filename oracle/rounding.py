@@ -43,10 +43,25 @@ def _as64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def _zr(keep, p, b, h):
+_ROW_BLOCK = 1024
+
+
+def _blocks(qh, kh, scale, causal):
+    """Row blocks of one head: (rows, visible key count c, P [rows, c]) from the oracle's own
+    scores and masked softmax, so no N_q x N_k matrix is formed at once."""
+    nq, nk = qh.shape[0], kh.shape[0]
+    for s0 in range(0, nq, _ROW_BLOCK):
+        r = np.arange(s0, min(nq, s0 + _ROW_BLOCK))
+        ncols = np.array([min(int(i) + 1, nk) if causal else nk for i in r])
+        c = int(ncols.max())
+        pm, _, _ = att.softmax_rows(att.scores(qh[r], kh[:c], scale), ncols)
+        yield r, c, pm
+
+
+def _zr(keep, p, b, h, r, c):
     if keep is None:
         return 1.0
-    return keep[b, h] * (256.0 / (256 - odp.threshold(p)))
+    return keep[b, h][r][:, :c] * (256.0 / (256 - odp.threshold(p)))
 
 
 def forward_terms(q, k, v, causal: bool = False, scale: float | None = None, keep=None, p: float = 0.0):
@@ -59,8 +74,8 @@ def forward_terms(q, k, v, causal: bool = False, scale: float | None = None, kee
     for b in range(B):
         for h in range(Hq):
             g = h // G
-            pd = att.probabilities(q[b, :, h], k[b, :, g], scale, causal) * _zr(keep, p, b, h)
-            t[b, :, h] = pd @ np.abs(v[b, :, g])
+            for r, c, pm in _blocks(q[b, :, h], k[b, :, g], scale, causal):
+                t[b, r, h] = (pm * _zr(keep, p, b, h, r, c)) @ np.abs(v[b, :c, g])
     return t
 
 
@@ -82,22 +97,23 @@ def backward_terms(q, k, v, do, causal: bool = False, scale: float | None = None
     for b in range(B):
         for h in range(Hq):
             g = h // G
-            pm = att.probabilities(q[b, :, h], k[b, :, g], scale, causal)
-            zr = _zr(keep, p, b, h)
-            pd = pm * zr
-            o = pd @ v[b, :, g]
-            t_o = pd @ np.abs(v[b, :, g])
-            e_do = (np.abs(do[b, :, h]) * np.abs(o)).sum(axis=1)
-            e_dp = (np.abs(do[b, :, h]) * t_o).sum(axis=1)
-            dpd = (do[b, :, h] @ v[b, :, g].T) * zr
-            ds = pm * (dpd - (pm * dpd).sum(axis=1, keepdims=True))
-            ak, aq = np.abs(k[b, :, g]), np.abs(q[b, :, h])
-            part["dV"]["P"][b, :, g] += pd.T @ np.abs(do[b, :, h])
-            part["dQ"]["dS"][b, :, h] = scale * (np.abs(ds) @ ak)
-            part["dK"]["dS"][b, :, g] += scale * (np.abs(ds).T @ aq)
-            for name, e in (("D_O", e_do), ("D_P", e_dp)):
-                part["dQ"][name][b, :, h] = scale * e[:, None] * (pm @ ak)
-                part["dK"][name][b, :, g] += scale * ((pm * e[:, None]).T @ aq)
+            for r, c, pm in _blocks(q[b, :, h], k[b, :, g], scale, causal):
+                zr = _zr(keep, p, b, h, r, c)
+                pd = pm * zr
+                vv, dor = v[b, :c, g], do[b, r, h]
+                o = pd @ vv
+                t_o = pd @ np.abs(vv)
+                e_do = (np.abs(dor) * np.abs(o)).sum(axis=1)
+                e_dp = (np.abs(dor) * t_o).sum(axis=1)
+                dpd = (dor @ vv.T) * zr
+                ds = pm * (dpd - (pm * dpd).sum(axis=1, keepdims=True))
+                ak, aq = np.abs(k[b, :c, g]), np.abs(q[b, r, h])
+                part["dV"]["P"][b, :c, g] += pd.T @ np.abs(dor)
+                part["dQ"]["dS"][b, r, h] = scale * (np.abs(ds) @ ak)
+                part["dK"]["dS"][b, :c, g] += scale * (np.abs(ds).T @ aq)
+                for name, e in (("D_O", e_do), ("D_P", e_dp)):
+                    part["dQ"][name][b, r, h] = scale * e[:, None] * (pm @ ak)
+                    part["dK"][name][b, :c, g] += scale * ((pm * e[:, None]).T @ aq)
     if parts:
         return part
     return tuple(sum(part[n].values()) for n in ("dQ", "dK", "dV"))

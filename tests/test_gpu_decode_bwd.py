@@ -9,6 +9,7 @@ import pytest
 import workloads
 from gpu_util import check, say, to_dev, to_np
 from oracle import attention as ora
+from oracle import rounding as rnd
 
 pytestmark = pytest.mark.gpu
 
@@ -180,6 +181,38 @@ def test_bwd_small(B, Nq, Nk, Hq, Hkv, d, causal, seed, single_pass):
     check("dQ", dq, rq, "bf16")
     check("dK", dk, rk, "bf16")
     check("dV", dv, rv, "bf16")
+
+
+@pytest.mark.parametrize("single_pass", [False, True])
+def test_bwd_255_key_blocks(single_pass):
+    # the largest key-block count the single pass takes (Nk = 32640, 8-bit adder tags): every
+    # block of dQ gets 255 adders, without the mask; the two-kernel path on the same inputs
+    B, Nq, Nk, Hq, Hkv, d = 1, 100, 32640, 2, 1, 128
+    say(f"bwd 255 key blocks B={B} Nq={Nq} Nk={Nk} Hq={Hq} Hkv={Hkv} single_pass={single_pass}")
+    inp = workloads.make_attention_inputs(B, Nq, Nk, Hq, Hkv, d, seed=5301, with_do=True)
+    # with 32640 keys every P is about 3e-5 and the gradients are small next to the 2e-2 floor;
+    # dO times 64 (exact in bf16) brings them to order one
+    inp["do"] = inp["do"] * 64.0
+    scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = run_fwd_bwd(inp, False, scale, single_pass=single_pass)
+    args = (inp["q"], inp["k"], inp["v"], inp["do"], False, scale)
+    for n, g, r, t in zip(("dQ", "dK", "dV"), (dq, dk, dv), ora.backward(*args), rnd.backward_terms(*args)):
+        check(n, g, r, "bf16", terms=t)
+
+
+@pytest.mark.parametrize("single_pass", [False, True])
+def test_bwd_long_causal(single_pass):
+    # one long causal head: 256 query blocks, 128 key blocks (the single pass's longest task
+    # walks 256 blocks; its shortest two)
+    B, N, Hq, Hkv, d = 1, 16384, 1, 1, 128
+    say(f"bwd long causal N={N} single_pass={single_pass}")
+    inp = workloads.make_attention_inputs(B, N, N, Hq, Hkv, d, seed=5302, with_do=True)
+    scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = run_fwd_bwd(inp, True, scale, single_pass=single_pass)
+    say("  oracle gradients and rounding terms")
+    args = (inp["q"], inp["k"], inp["v"], inp["do"], True, scale)
+    for n, g, r, t in zip(("dQ", "dK", "dV"), (dq, dk, dv), ora.backward(*args), rnd.backward_terms(*args)):
+        check(n, g, r, "bf16", terms=t)
 
 
 @pytest.mark.parametrize("single_pass", [False, True])
