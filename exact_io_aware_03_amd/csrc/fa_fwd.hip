@@ -167,14 +167,20 @@ template <int D, bool F8>
 __device__ __forceinline__ void dma_tile(char* buf, const char* kp, const char* vp, long k_row, int kv0, int nk,
                                          const TileDma<D, F8>& dm) {
   using T = Tile<D, F8>;
-  const long valid = (long)(nk - 1 - kv0) * k_row + D;  // values up to the end of the last row
-  const u32x4 rk = dma_rsrc(kp + (long)kv0 * k_row * T::KE, valid * T::KE);
-  const u32x4 rv = dma_rsrc(vp + (long)kv0 * k_row * 2, valid * 2);
-  const int w = threadIdx.x >> 6;
+  // one resource over the whole head (the same for every tile, so it is formed once): values up
+  // to the end of the last row; the tile's start goes into the per-lane offset, which the
+  // range check covers, so keys at or past nk still read as zeros. The host keeps a head's K
+  // and V below 2^31 bytes, so offset + tile start fits 32 bits unsigned (the padding rows'
+  // offset included, which stays out of range)
+  const long valid = (long)(nk - 1) * k_row + D;
+  const u32x4 rk = dma_rsrc(kp, valid * T::KE);
+  const u32x4 rv = dma_rsrc(vp, valid * 2);
+  const uint32_t tk = (uint32_t)((long)kv0 * k_row * T::KE), tv = (uint32_t)((long)kv0 * k_row * 2);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int p = 0; p < T::VDMA; ++p) {
-    if (p < T::KDMA) lds_dma16(rk, buf + (kWaves * p + w) * 1024, dm.k_off[p]);
-    lds_dma16(rv, buf + T::K_BYTES + (kWaves * p + w) * 1024, dm.v_off[p]);
+    if (p < T::KDMA) lds_dma16(rk, buf + (kWaves * p + w) * 1024, (int)((uint32_t)dm.k_off[p] + tk));
+    lds_dma16(rv, buf + T::K_BYTES + (kWaves * p + w) * 1024, (int)((uint32_t)dm.v_off[p] + tv));
   }
 }
 
